@@ -1,0 +1,138 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged-KV-cache decode attention for MI355X (gfx950).
+ *
+ * The KV cache of every sequence is split into fixed-size physical blocks that
+ * may sit anywhere in one pool; a per-sequence Block Table maps logical block j
+ * to its physical block id ("PagedAttention核心思想", sections 2.2-2.3; CSDN
+ * answer "VLLM中PagedAttention如何降低显存碎片？", section 三 items 1-4).
+ *
+ * Layouts (row-major, element counts):
+ *   k_cache, v_cache  [num_blocks, num_kv_heads, block_size, head_dim]
+ *                     one block holds block_size tokens for every KV head
+ *                     ("PagedAttention核心思想" section 2.3)
+ *   block_tables      int32 [num_seqs, max_blocks_per_seq]; entry [i][j] is the
+ *                     physical block holding tokens [j*block_size, (j+1)*block_size)
+ *                     of sequence i.  Entries j >= ceil(context_lens[i]/block_size)
+ *                     are never read.
+ *   context_lens      int32 [num_seqs]; tokens attended by sequence i
+ *   q, out            [num_seqs, num_q_heads, head_dim], contiguous
+ *   k, v (new tokens) [num_tokens, num_kv_heads, head_dim]; tokens may be strided
+ *   slot_mapping      int64 [num_tokens]; slot = physical_block*block_size + offset
+ *
+ * Ownership: every pointer argument is device memory owned by the caller.  The
+ * library allocates nothing, keeps no mutable global state and is reentrant; all
+ * work is queued asynchronously on `stream` (NULL = the null stream).  Outputs
+ * are `out` and the caches; `out` must not alias q or the caches, and k/v must
+ * not alias the caches.
+ *
+ * Errors: every call returns a pkv_status_t.  Arguments are checked on the host
+ * only (no device reads, no synchronisation); a failed check returns before
+ * anything is launched.  Preconditions on device-resident data are NOT checked:
+ * block ids used by a sequence lie in [0, num_blocks); non-negative slots are
+ * distinct and below num_blocks*block_size; 0 <= context_lens[i] <= max_context_len.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, out, k, v and the caches. */
+typedef enum pkv_dtype {
+    PKV_F32 = 0,
+    PKV_F16 = 1,
+    PKV_BF16 = 2
+} pkv_dtype_t;
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    PKV_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree          */
+    PKV_ERR_DTYPE = 3,       /* unknown dtype code                                */
+    PKV_ERR_UNSUPPORTED = 4, /* valid, but no kernel is built for it (head_dim,   */
+                             /* block size or query-per-KV-head group)            */
+    PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
+    PKV_ERR_ALIGN = 6,       /* a pointer or token stride is not 16-byte aligned  */
+    PKV_ERR_HIP = 7          /* the HIP runtime reported an error at launch       */
+} pkv_status_t;
+
+/* Static text for a status code (never NULL). */
+const char *pkv_status_string(int status);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int pkv_version(void);
+
+/*
+ * paged_kv_write -- append new tokens' K/V to the paged cache.
+ *
+ * For every token n with slot s = slot_mapping[n] >= 0 and every KV head h:
+ *   k_cache[s / block_size, h, s % block_size, :] = k[n, h, :]   (bit copy)
+ *   v_cache[s / block_size, h, s % block_size, :] = v[n, h, :]
+ * A negative slot skips the token.  Defined by "PagedAttention核心思想" section
+ * 2.4.2 (a new token goes into the next slot of the last block; a fresh block
+ * is taken only when the last one is full) and the CSDN answer's flow chart in
+ * section 四 (append a page, update the mapping).
+ *
+ *   k, v             new tokens, element (n, h, d) at n*token_stride + h*head_dim + d
+ *   k_token_stride,
+ *   v_token_stride   elements between consecutive tokens (>= num_kv_heads*head_dim)
+ *   num_tokens       may be 0 (nothing is launched)
+ *   head_dim         64 or 128;  block_size > 0;  num_blocks > 0
+ * Pointers and strides in bytes must be multiples of 16.
+ */
+int paged_kv_write(const void *k, const void *v, void *k_cache, void *v_cache,
+                   const int64_t *slot_mapping, int64_t num_tokens,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int64_t num_blocks, int64_t k_token_stride, int64_t v_token_stride,
+                   int32_t dtype, hipStream_t stream);
+
+/*
+ * Bytes of device workspace paged_attn_decode needs for these sizes (0 when a
+ * single pass suffices).  Long contexts are split into partitions whose
+ * partial results (running max, exp-sum, un-normalised output; fp32) are kept
+ * here and merged by a second kernel.  Returns 0 for invalid sizes too; the
+ * decode call reports those.
+ */
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_context_len);
+
+/*
+ * paged_attn_decode -- one query token per sequence attends over its paged KV cache.
+ *
+ * For sequence i and query head h (KV head g = h / (num_q_heads/num_kv_heads)):
+ *   s_t = scale * dot(q[i,h,:], K_t)      t in [0, context_lens[i])
+ *   out[i,h,:] = sum_t softmax(s)_t * V_t
+ * where K_t, V_t are row t % block_size of KV head g in physical block
+ * block_tables[i][t / block_size].  The table is walked inside the kernel,
+ * block by block, with a numerically stable (running-max) softmax
+ * ("PagedAttention核心思想" section 2.5; "PagedAttention技术解析" sections 2.2
+ * and 3.1; CSDN answer section 三 items 4-6 and 9, and section 四 on the
+ * partitioned second version).  Slots past context_lens[i] in the last block
+ * are never used.  context_lens[i] == 0 gives out[i] = 0.  Accumulation is
+ * fp32; out is rounded once to its dtype (round to nearest even).
+ *
+ *   num_q_heads % num_kv_heads == 0 and the group size is 1, 2, 4 or 8
+ *   head_dim 64 or 128; block_size a multiple of 16 up to 256
+ *   max_blocks_per_seq*block_size >= max_context_len
+ *   workspace: >= paged_attn_decode_workspace_size(...) bytes of device memory
+ *              (may be NULL when that size is 0); contents need not be initialised
+ */
+int paged_attn_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                      int64_t num_blocks, int32_t max_context_len, float scale,
+                      int32_t dtype, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,170 @@
+"""ctypes binding of libpkv.so.
+
+Argument marshalling only: shapes and dtypes are read off torch tensors, and the
+device pointers, sizes and the current HIP stream are handed to the C entry
+points declared in ``include/pkv.h``.  Every step of the computation runs in the
+library's kernels.  The library is loaded on first use; if it has not been built
+the call raises -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libpkv.so"
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+_lock = threading.Lock()
+_lib: Optional[ctypes.CDLL] = None
+
+
+class PKVError(RuntimeError):
+    """A libpkv call returned a non-zero status."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libpkv error {status}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("PKV_LIBRARY", os.path.join(_HERE, LIB_NAME))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libpkv.so (once).  torch is imported first so that the HIP runtime
+    torch ships is the one the library binds to (same soname)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "or `python -m paged_kv_cache_353_amd.build` first")
+        lib = ctypes.CDLL(path)
+        c_int, c_i32, c_i64, c_sz, c_p, c_f = (ctypes.c_int, ctypes.c_int32, ctypes.c_int64,
+                                               ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float)
+        lib.pkv_status_string.argtypes = [c_int]
+        lib.pkv_status_string.restype = ctypes.c_char_p
+        lib.pkv_version.argtypes = []
+        lib.pkv_version.restype = c_int
+        lib.paged_kv_write.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i32, c_i32, c_i32,
+                                       c_i64, c_i64, c_i64, c_i32, c_p]
+        lib.paged_kv_write.restype = c_int
+        lib.paged_attn_decode_workspace_size.argtypes = [c_i32] * 6
+        lib.paged_attn_decode_workspace_size.restype = c_sz
+        lib.paged_attn_decode.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32,
+                                          c_i32, c_i32, c_i32, c_i64, c_i32, c_f, c_i32,
+                                          c_p, c_sz, c_p]
+        lib.paged_attn_decode.restype = c_int
+        _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        raise PKVError(status, lib.pkv_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE_CODE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def paged_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                   v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Scatter new tokens' K/V ([num_tokens, num_kv_heads, head_dim]) into the
+    paged caches at ``slot_mapping`` (int64; negative = skip).  Asynchronous on
+    the current stream of the caches' device."""
+    if k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("k and v must both be [num_tokens, num_kv_heads, head_dim]")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k, v and the caches must share one dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or slot_mapping.numel() != k.shape[0]:
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    for t in (k, v):
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError("k/v rows must be contiguous within a token")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous() and slot_mapping.is_contiguous()):
+        raise ValueError("caches and slot_mapping must be contiguous")
+    nb, hkv, bs, d = k_cache.shape
+    lib = load_library()
+    with torch.cuda.device(k_cache.device):
+        _check(lib.paged_kv_write(
+            k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            slot_mapping.data_ptr(), k.shape[0], hkv, d, bs, nb, k.stride(0), v.stride(0),
+            _dtype_code(k_cache), _stream_handle(k_cache.device)))
+
+
+def paged_attn_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                     head_dim: int, block_size: int, max_context_len: int) -> int:
+    lib = load_library()
+    return int(lib.paged_attn_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                    head_dim, block_size, max_context_len))
+
+
+def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, block_size: int, scale: float,
+                      max_context_len: Optional[int] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention of one query token per sequence over the paged cache.
+
+    ``out``/``q``: [num_seqs, num_q_heads, head_dim]; caches
+    [num_blocks, num_kv_heads, block_size, head_dim]; ``block_tables`` int32
+    [num_seqs, max_blocks_per_seq]; ``context_lens`` int32 [num_seqs].
+    ``max_context_len`` defaults to ``max_blocks_per_seq * block_size`` (an
+    upper bound that needs no device read); a tighter value shrinks the
+    launch.  ``workspace`` (uint8, on the device) is allocated through torch
+    when not given.  Returns ``out``.
+    """
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != q.shape[0] or context_lens.shape != (q.shape[0],):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
+    for t in (out, q, k_cache, v_cache, block_tables, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if int(block_size) != k_cache.shape[2]:
+        raise ValueError("block_size must equal k_cache.shape[2]")
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    mb = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mb * bs
+    lib = load_library()
+    need = int(lib.paged_attn_decode_workspace_size(S, hq, hkv, d, bs, int(max_context_len)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.paged_attn_decode(
+            out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), S, hq, hkv, d, bs, mb, nb,
+            int(max_context_len), float(scale), _dtype_code(q),
+            workspace.data_ptr() if workspace.numel() else None, workspace.numel(),
+            _stream_handle(q.device)))
+    return out

@@ -1,0 +1,381 @@
+"""Pins for the fp64 oracle: each check comes from something other than the
+oracle itself (the pages' worked examples, a library routine, brute force,
+closed forms, invariances the pages state)."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gather_rows, paged_attn_decode, paged_kv_write, physical_slot, to_f64
+from tests.paging_helpers import brute_force_decode, page_in
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_problem(rng, lens, Hq, Hkv, D, bs, num_blocks):
+    q = rng.standard_normal((len(lens), Hq, D))
+    lk = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    lv = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    order = rng.permutation(num_blocks)
+    kp, vp, tables = page_in(lk, lv, lens, bs, num_blocks, order)
+    return q, lk, lv, kp, vp, tables
+
+
+def _f32(x):
+    """Round to float32 storage so the oracle reads exactly these values."""
+    return np.asarray(x, dtype=np.float32)
+
+
+# ---------------------------------------------------------------------------
+# stored-value decoding (IEEE binary16 / bfloat16 definitions)
+# ---------------------------------------------------------------------------
+
+def test_decode_bf16_bit_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F80, 0x4049], dtype=np.uint16)
+    got = to_f64(bits, "bf16")
+    want = [1.0, -2.0, 1.0 + 2.0 ** -7, 0.0, -0.0, math.inf, 3.140625]
+    assert got.tolist() == want
+    assert math.copysign(1.0, got[4]) == -1.0
+
+
+def test_decode_fp16_bit_patterns():
+    bits = np.array([0x3C00, 0xC000, 0x3C01, 0x7BFF, 0x0001], dtype=np.uint16)
+    got = to_f64(bits, "f16")
+    assert got.tolist() == [1.0, -2.0, 1.0 + 2.0 ** -10, 65504.0, 2.0 ** -24]
+
+
+def test_decode_bf16_matches_torch():
+    x = torch.randn(1000, dtype=torch.float32).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(to_f64(bits, "bf16"), x.to(torch.float64).numpy())
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked mapping examples (golden fixture)
+# ---------------------------------------------------------------------------
+
+def _golden_pool(fx):
+    NB, H, BS, D = fx["num_blocks"], fx["num_kv_heads"], fx["block_size"], fx["head_dim"]
+    k = np.zeros((NB, H, BS, D), dtype=np.float32)
+    for b in range(NB):
+        for h in range(H):
+            for o in range(BS):
+                for d in range(D):
+                    k[b, h, o, d] = 1000 * b + 100 * h + o + d / 128.0
+    return k, -k
+
+
+def test_golden_block_table_examples():
+    with open(os.path.join(GOLDEN, "block_table_examples.json")) as f:
+        fx = json.load(f)
+    k, v = _golden_pool(fx)
+    bs = fx["block_size"]
+    for case in fx["cases"]:
+        table = np.array(case["table"])
+        L = case["context_len"]
+        assert len(case["expected_rows"]) == L
+        for t, (blk, off) in enumerate(case["expected_rows"]):
+            assert physical_slot(table, t, bs) == (blk, off)
+        for h in range(fx["num_kv_heads"]):
+            got = gather_rows(k, table, h, 0, L, bs, "f32")
+            want = np.array([k[b, h, o] for b, o in case["expected_rows"]], dtype=np.float64)
+            assert np.array_equal(got, want)
+            gotv = gather_rows(v, table, h, 0, L, bs, "f32")
+            assert np.array_equal(gotv, -want)
+
+
+def test_golden_block_bytes():
+    with open(os.path.join(GOLDEN, "block_bytes.json")) as f:
+        fx = json.load(f)
+    for c in fx["block_bytes_cases"]:
+        dt = {2: torch.bfloat16, 4: torch.float32}[c["dtype_bytes"]]
+        kc = torch.empty((3, c["num_kv_heads"], c["block_size"], c["head_dim"]), dtype=dt)
+        vc = torch.empty_like(kc)
+        assert kc[0].numel() * kc.element_size() + vc[0].numel() * vc.element_size() == c["bytes"]
+
+
+# ---------------------------------------------------------------------------
+# paged result == dense attention over the logical sequence (library routine)
+# ---------------------------------------------------------------------------
+
+def _sdpa_reference(q, lk, lv, scale, group):
+    """torch's scaled_dot_product_attention in float64 on the logical arrays."""
+    S, Hq, D = q.shape
+    out = np.zeros((S, Hq, D))
+    for i in range(S):
+        if lk[i].shape[0] == 0:
+            continue
+        K = torch.from_numpy(lk[i]).permute(1, 0, 2)  # [Hkv, L, D]
+        V = torch.from_numpy(lv[i]).permute(1, 0, 2)
+        K = K.repeat_interleave(group, dim=0).unsqueeze(0)
+        V = V.repeat_interleave(group, dim=0).unsqueeze(0)
+        Q = torch.from_numpy(q[i]).unsqueeze(0).unsqueeze(2)  # [1, Hq, 1, D]
+        o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=scale)
+        out[i] = o[0, :, 0, :].numpy()
+    return out
+
+
+@pytest.mark.parametrize("Hq,Hkv,bs", [(4, 4, 16), (8, 2, 16), (8, 2, 4), (6, 3, 32), (8, 1, 1)])
+def test_paged_equals_dense_sdpa(Hq, Hkv, bs):
+    rng = np.random.default_rng(11 + Hq + bs)
+    lens = [1, 17, 48, 93]
+    D = 16
+    q, lk, lv, kp, vp, tables = _rand_problem(rng, lens, Hq, Hkv, D, bs, 200)
+    # store in fp32 so the stored values are what both sides read
+    q32, kp32, vp32 = _f32(q), _f32(kp), _f32(vp)
+    lk32 = [to_f64(_f32(x), "f32") for x in lk]
+    lv32 = [to_f64(_f32(x), "f32") for x in lv]
+    scale = 1 / math.sqrt(D)
+    got = paged_attn_decode(q32, kp32, vp32, tables, np.array(lens), bs, scale, "f32")
+    want = _sdpa_reference(to_f64(q32, "f32"), lk32, lv32, scale, Hq // Hkv)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_brute_force_tiny():
+    rng = np.random.default_rng(5)
+    for group in (1, 2):
+        lens = [1, 9, 40]
+        Hkv, D = 2, 8
+        Hq = Hkv * group
+        q, lk, lv, kp, vp, tables = _rand_problem(rng, lens, Hq, Hkv, D, 4, 20)
+        q32, kp32, vp32 = _f32(q), _f32(kp), _f32(vp)
+        lk64 = [to_f64(_f32(x), "f32").tolist() for x in lk]
+        lv64 = [to_f64(_f32(x), "f32").tolist() for x in lv]
+        got = paged_attn_decode(q32, kp32, vp32, tables, np.array(lens), 4, 0.37, "f32")
+        want = brute_force_decode(to_f64(q32, "f32").tolist(), lk64, lv64, 0.37, group)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# invariances the pages state
+# ---------------------------------------------------------------------------
+
+def test_physical_permutation_invariance_bitwise():
+    """Relabelling physical blocks (the 7/3/12 argument) changes nothing."""
+    rng = np.random.default_rng(7)
+    lens = [33, 40, 48, 5]
+    q, lk, lv, kp, vp, tables = _rand_problem(rng, lens, 8, 2, 32, 16, 40)
+    kp, vp, q = _f32(kp), _f32(vp), _f32(q)
+    base = paged_attn_decode(q, kp, vp, tables, np.array(lens), 16, 0.2, "f32")
+    pi = rng.permutation(40)
+    kp2 = np.empty_like(kp)
+    vp2 = np.empty_like(vp)
+    kp2[pi] = kp
+    vp2[pi] = vp
+    got = paged_attn_decode(q, kp2, vp2, pi[tables], np.array(lens), 16, 0.2, "f32")
+    assert np.array_equal(got, base)
+
+
+def test_shared_prefix_equals_private_copies_bitwise():
+    """Tables pointing at the same physical prefix blocks == private copies."""
+    rng = np.random.default_rng(8)
+    bs, Hkv, D, Hq = 16, 2, 16, 4
+    prefix = rng.standard_normal((48, Hkv, D)).astype(np.float32)
+    forks = 4
+    lk = [np.concatenate([prefix, rng.standard_normal((20, Hkv, D)).astype(np.float32)]) for _ in range(forks)]
+    lv = [np.concatenate([-prefix, rng.standard_normal((20, Hkv, D)).astype(np.float32)]) for _ in range(forks)]
+    lens = [68] * forks
+    q = _f32(rng.standard_normal((forks, Hq, D)))
+    # private copies
+    kp, vp, tables = page_in(lk, lv, lens, bs, 64, rng.permutation(64))
+    private = paged_attn_decode(q, _f32(kp), _f32(vp), tables, np.array(lens), bs, 0.25, "f32")
+    # shared: the 3 prefix blocks of fork 0 serve every fork
+    shared_tables = tables.copy()
+    shared_tables[:, :3] = tables[0, :3]
+    shared = paged_attn_decode(q, _f32(kp), _f32(vp), shared_tables, np.array(lens), bs, 0.25, "f32")
+    assert np.array_equal(shared, private)
+
+
+def test_block_size_independence():
+    rng = np.random.default_rng(9)
+    lens = [1, 31, 64, 100]
+    Hkv, D = 2, 16
+    q = _f32(rng.standard_normal((4, 4, D)))
+    lk = [rng.standard_normal((L, Hkv, D)).astype(np.float32) for L in lens]
+    lv = [rng.standard_normal((L, Hkv, D)).astype(np.float32) for L in lens]
+    outs = []
+    for bs in (1, 4, 16, 32, 128):
+        nb = sum(-(-L // bs) for L in lens) + 3
+        kp, vp, tables = page_in(lk, lv, lens, bs, nb, rng.permutation(nb))
+        outs.append(paged_attn_decode(q, _f32(kp), _f32(vp), tables, np.array(lens), bs, 0.3, "f32"))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_probabilities_sum_to_one():
+    rng = np.random.default_rng(10)
+    lens = [1, 77, 300]
+    q, lk, lv, kp, vp, tables = _rand_problem(rng, lens, 4, 2, 16, 16, 40)
+    out, probs = paged_attn_decode(_f32(q), _f32(kp), _f32(vp), tables, np.array(lens), 16,
+                                   1.0, "f32", return_probs=True)
+    for (i, h), p in probs.items():
+        assert p.shape == (lens[i],)
+        assert np.all(p >= 0)
+        assert abs(p.sum() - 1.0) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# closed forms and degenerate cases
+# ---------------------------------------------------------------------------
+
+def test_single_token_returns_its_value_exactly():
+    rng = np.random.default_rng(12)
+    q, lk, lv, kp, vp, tables = _rand_problem(rng, [1, 1], 4, 4, 8, 16, 4)
+    kp, vp = _f32(kp), _f32(vp)
+    out = paged_attn_decode(_f32(q), kp, vp, tables, np.array([1, 1]), 16, 0.5, "f32")
+    for i in range(2):
+        for h in range(4):
+            assert np.array_equal(out[i, h], vp[tables[i, 0], h, 0].astype(np.float64))
+
+
+@pytest.mark.parametrize("mode", ["zero_q", "zero_scale", "equal_keys"])
+def test_uniform_weights_give_mean_of_values(mode):
+    rng = np.random.default_rng(13)
+    lens = [37, 64]
+    q, lk, lv, kp, vp, tables = _rand_problem(rng, lens, 2, 1, 8, 16, 10)
+    scale = 0.7
+    if mode == "zero_q":
+        q = np.zeros_like(q)
+    if mode == "zero_scale":
+        scale = 0.0
+    if mode == "equal_keys":
+        kp[...] = 1.25
+    out = paged_attn_decode(_f32(q), _f32(kp), _f32(vp), tables, np.array(lens), 16, scale, "f32")
+    for i, L in enumerate(lens):
+        mean = to_f64(_f32(lv[i]), "f32")[:, 0, :].mean(axis=0)
+        for h in range(2):
+            np.testing.assert_allclose(out[i, h], mean, rtol=1e-13, atol=1e-15)
+
+
+def test_dominant_key_selects_its_value():
+    rng = np.random.default_rng(14)
+    L, D = 50, 8
+    lk = [np.zeros((L, 1, D))]
+    lv = [rng.standard_normal((L, 1, D))]
+    star = 23
+    lk[0][star, 0, 0] = 80.0   # score gap of 80 over every other key (q = e0)
+    kp, vp, tables = page_in(lk, lv, [L], 16, 8, rng.permutation(8))
+    q = np.zeros((1, 1, D))
+    q[0, 0, 0] = 1.0
+    out = paged_attn_decode(_f32(q), _f32(kp), _f32(vp), tables, np.array([L]), 16, 1.0, "f32")
+    want = to_f64(_f32(lv[0][star, 0]), "f32")
+    np.testing.assert_allclose(out[0, 0], want, rtol=1e-30, atol=1e-30 + 1e-33)
+    assert np.max(np.abs(out[0, 0] - want)) <= 1e-30 + np.max(np.abs(want)) * 1e-30
+
+
+def test_zero_context_gives_zero_output():
+    rng = np.random.default_rng(15)
+    q, lk, lv, kp, vp, tables = _rand_problem(rng, [0, 5], 2, 2, 8, 16, 4)
+    out = paged_attn_decode(_f32(q), _f32(kp), _f32(vp), tables, np.array([0, 5]), 16, 1.0, "f32")
+    assert np.array_equal(out[0], np.zeros((2, 8)))
+    assert np.all(np.isfinite(out[1]))
+
+
+def test_gqa_mapping_contiguous_groups():
+    """Query head h reads KV head h // (Hq/Hkv): each KV head's V is a constant."""
+    Hkv, G, D, L = 4, 2, 8, 20
+    lk = [np.zeros((L, Hkv, D))]
+    lv = [np.zeros((L, Hkv, D))]
+    for g in range(Hkv):
+        lv[0][:, g, :] = g + 1
+    kp, vp, tables = page_in(lk, lv, [L], 16, 4, np.arange(4))
+    q = np.ones((1, Hkv * G, D))
+    out = paged_attn_decode(_f32(q), _f32(kp), _f32(vp), tables, np.array([L]), 16, 1.0, "f32")
+    for h in range(Hkv * G):
+        np.testing.assert_allclose(out[0, h], np.full(D, h // G + 1.0), rtol=1e-14)
+
+
+def test_poison_in_unread_slots_does_not_leak():
+    """NaN in unused blocks, tails and padding vs zeros there: identical."""
+    rng = np.random.default_rng(16)
+    lens = [17, 40, 3]
+    q = _f32(rng.standard_normal((3, 4, 16)))
+    lk = [rng.standard_normal((L, 2, 16)) for L in lens]
+    lv = [rng.standard_normal((L, 2, 16)) for L in lens]
+    order = rng.permutation(12)
+    kn, vn, tables = page_in(lk, lv, lens, 16, 12, order, fill=np.nan)
+    kz, vz, _ = page_in(lk, lv, lens, 16, 12, order, fill=0.0)
+    a = paged_attn_decode(q, _f32(kn), _f32(vn), tables, np.array(lens), 16, 0.25, "f32")
+    b = paged_attn_decode(q, _f32(kz), _f32(vz), tables, np.array(lens), 16, 0.25, "f32")
+    assert np.all(np.isfinite(a))
+    assert np.array_equal(a, b)
+
+
+def test_sampled_pairs_match_full():
+    rng = np.random.default_rng(17)
+    lens = [20, 70]
+    q, lk, lv, kp, vp, tables = _rand_problem(rng, lens, 4, 2, 8, 16, 12)
+    full = paged_attn_decode(_f32(q), _f32(kp), _f32(vp), tables, np.array(lens), 16, 0.5, "f32")
+    part = paged_attn_decode(_f32(q), _f32(kp), _f32(vp), tables, np.array(lens), 16, 0.5, "f32",
+                             pairs=[(1, 3), (0, 0)])
+    assert np.array_equal(part[1, 3], full[1, 3])
+    assert np.array_equal(part[0, 0], full[0, 0])
+    assert np.isnan(part[0, 1]).all()
+
+
+def test_chunked_long_sequence_matches_unchunked():
+    rng = np.random.default_rng(18)
+    lens = [1000]
+    q, lk, lv, kp, vp, tables = _rand_problem(rng, lens, 2, 1, 8, 16, 70)
+    a = paged_attn_decode(_f32(q), _f32(kp), _f32(vp), tables, np.array(lens), 16, 0.5, "f32")
+    b = paged_attn_decode(_f32(q), _f32(kp), _f32(vp), tables, np.array(lens), 16, 0.5, "f32",
+                          chunk_tokens=48)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
+
+
+def test_bf16_storage_path_equals_upcast_f32():
+    rng = np.random.default_rng(19)
+    lens = [30, 45]
+    q, lk, lv, kp, vp, tables = _rand_problem(rng, lens, 4, 2, 16, 16, 10)
+    tq = torch.from_numpy(q).float().to(torch.bfloat16)
+    tk = torch.from_numpy(kp).float().to(torch.bfloat16)
+    tv = torch.from_numpy(vp).float().to(torch.bfloat16)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    a = paged_attn_decode(bits(tq), bits(tk), bits(tv), tables, np.array(lens), 16, 0.25, "bf16")
+    b = paged_attn_decode(tq.float().numpy(), tk.float().numpy(), tv.float().numpy(), tables,
+                          np.array(lens), 16, 0.25, "f32")
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# KV append
+# ---------------------------------------------------------------------------
+
+def test_kv_write_round_trip_and_untouched_bytes():
+    rng = np.random.default_rng(20)
+    NB, H, BS, D = 6, 2, 16, 8
+    kc = rng.standard_normal((NB, H, BS, D)).astype(np.float32)
+    vc = rng.standard_normal((NB, H, BS, D)).astype(np.float32)
+    N = 10
+    k = rng.standard_normal((N, H, D)).astype(np.float32)
+    v = rng.standard_normal((N, H, D)).astype(np.float32)
+    slots = rng.choice(NB * BS, size=N, replace=False).astype(np.int64)
+    slots[3] = -1
+    kc2, vc2 = paged_kv_write(k, v, kc, vc, slots)
+    written = np.zeros((NB, BS), dtype=bool)
+    for n, s in enumerate(slots):
+        if s < 0:
+            continue
+        b, o = divmod(int(s), BS)
+        written[b, o] = True
+        assert kc2[b, :, o, :].tobytes() == k[n].tobytes()
+        assert vc2[b, :, o, :].tobytes() == v[n].tobytes()
+    for b in range(NB):
+        for o in range(BS):
+            if not written[b, o]:
+                assert kc2[b, :, o].tobytes() == kc[b, :, o].tobytes()
+                assert vc2[b, :, o].tobytes() == vc[b, :, o].tobytes()
+    # the inputs are not modified
+    assert not np.shares_memory(kc2, kc)
+
+
+def test_kv_write_preserves_nan_payloads_and_signed_zero():
+    NB, H, BS, D = 2, 1, 16, 4
+    kc = np.zeros((NB, H, BS, D), dtype=np.uint16)
+    k = np.array([[[0x7FC1, 0x8000, 0xFF80, 0x0001]]], dtype=np.uint16)
+    kc2, _ = paged_kv_write(k, k, kc, kc, [17])
+    assert kc2[1, 0, 1].tolist() == [0x7FC1, 0x8000, 0xFF80, 0x0001]
