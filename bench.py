@@ -1,0 +1,284 @@
+"""Benchmark of the paged decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: append each
+sequence's new token to the paged cache (paged_kv_write), then decode
+attention of one query token per sequence over its cache (paged_attn_decode).
+The default workload is the Llama-8B-shaped batch: 64 sequences with context
+lengths uniform in [128, 2048], 32 query / 8 KV heads, head_dim 128, block
+size 16, bf16, blocks shuffled through an 8192-block pool.
+
+Inputs are resident in HBM before timing starts.  Steps rotate over several
+copies of the pool so that the data a step reads was last touched several
+steps (>1 GB of other traffic) earlier and has left the 256 MiB Infinity
+Cache: the timed bytes come from HBM.
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+METRIC = "decode-attn KV-read GB/s and % of MI355X HBM peak; query tokens/s"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["paged_kv_cache_353_amd/csrc/attn_decode.hip"]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def build_workload(name: str, dev: str):
+    from paged_kv_cache_353_amd import workloads as W
+    if name == "llama8b":
+        return W.llama8b_decode(dev)
+    if name.startswith("sweep"):
+        return W.block_size_sweep(int(name[len("sweep"):] or 16), dev)
+    if name == "shared_prefix":
+        return W.shared_prefix(dev)
+    if name == "long_context":
+        return W.long_context(dev)
+    if name == "tiny":
+        return W.tiny(dev)
+    raise SystemExit(f"unknown workload {name!r}")
+
+
+def replicas(inp, n: int):
+    """n input sets with the same values at distinct HBM addresses."""
+    from paged_kv_cache_353_amd.workloads import DecodeInputs
+    sets = [inp]
+    for _ in range(n - 1):
+        sets.append(DecodeInputs(**{**inp.__dict__, "k_cache": inp.k_cache.clone(),
+                                    "v_cache": inp.v_cache.clone()}))
+    return sets
+
+
+def traffic_for(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
+    None when absent or taken on an older version of the kernel source."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(workload)
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def parity_check(inp, out, pairs):
+    """Sampled outputs of the timed data against the fp64 oracle (CPU)."""
+    import numpy as np
+    import oracle
+    from paged_kv_cache_353_amd.workloads import to_numpy_bits
+    q = to_numpy_bits(inp.q)
+    kc = to_numpy_bits(inp.k_cache)
+    vc = to_numpy_bits(inp.v_cache)
+    want = oracle.paged_attn_decode(q, kc, vc, inp.block_tables.cpu().numpy(),
+                                    inp.context_lens.cpu().numpy(), inp.block_size, inp.scale,
+                                    inp.dtype, pairs=pairs)
+    got = out.float().cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for i, h in pairs:
+        d = np.abs(got[i, h] - want[i, h])
+        if not np.all(d <= 2e-3 + 1e-2 * np.abs(want[i, h])):
+            raise SystemExit(f"parity check failed at seq {i} head {h}: max |d| {d.max():.3e}")
+        worst = max(worst, float(np.linalg.norm(got[i, h] - want[i, h]) / np.linalg.norm(want[i, h])))
+    return worst
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The fp64 oracle timed on this host's cores over the first n sequences
+    of the same workload (append + decode, every query head)."""
+    import numpy as np
+    import oracle
+    from paged_kv_cache_353_amd.workloads import to_numpy_bits
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q = to_numpy_bits(inp.q)
+    kc = to_numpy_bits(inp.k_cache)
+    vc = to_numpy_bits(inp.v_cache)
+    kn, vn = to_numpy_bits(inp.k_new), to_numpy_bits(inp.v_new)
+    tables = inp.block_tables.cpu().numpy()
+    lens = inp.context_lens.cpu().numpy()
+    slots = inp.slot_mapping.cpu().numpy()
+    Hq = inp.num_q_heads
+    done, tokens, t_total = 0, 0, 0.0
+    t0 = time.perf_counter()
+    kc2, vc2 = oracle.paged_kv_write(kn, vn, kc, vc, slots)
+    t_write = time.perf_counter() - t0
+    t_total += t_write
+    while done < inp.num_seqs and t_total < budget_s:
+        t0 = time.perf_counter()
+        oracle.paged_attn_decode(q, kc2, vc2, tables, lens, inp.block_size, inp.scale, inp.dtype,
+                                 pairs=[(done, h) for h in range(Hq)])
+        t_total += time.perf_counter() - t0
+        tokens += int(lens[done])
+        done += 1
+    kv_bytes = tokens * inp.num_kv_heads * inp.head_dim * 2 * (4 if inp.dtype == "f32" else 2)
+    return {"value": done / t_total, "unit": "query tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"first {done} of {inp.num_seqs} sequences of the same workload "
+                       f"(append + decode, all {Hq} query heads; the append copies the whole "
+                       f"pool once), {t_total:.1f} s on {len(os.sched_getaffinity(0))} host cores"),
+            "kv_read_gbs": kv_bytes / t_total / 1e9,
+            "seconds": t_total}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--sets", type=int, default=4, help="rotating input copies (cold-cache timing)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}): "
+              "the decode path is measured on a single MI355X; see the design notes for how "
+              "it would shard.", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_353_amd as pkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    pkv.load_library()
+    print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
+    base = build_workload(args.workload, dev)
+    nsets = max(1, args.sets if args.workload != "long_context" else 1)
+    sets = replicas(base, nsets)
+    S, Hq, Hkv, D = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_dim
+    maxL = base.max_context_len
+    ws_bytes = pkv.paged_attn_decode_workspace_size(S, Hq, Hkv, D, base.block_size, maxL)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(s.q) for s in sets]
+    kv_bytes = base.kv_read_bytes()
+    stream = torch.cuda.current_stream()
+
+    def step(s, out):
+        pkv.paged_kv_write(s.k_new, s.v_new, s.k_cache, s.v_cache, s.slot_mapping)
+        pkv.paged_attn_decode(out, s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
+                              s.block_size, s.scale, max_context_len=maxL, workspace=workspace)
+
+    # parity of the timed data, before timing
+    step(sets[0], outs[0])
+    torch.cuda.synchronize()
+    worst = None
+    if not args.no_parity:
+        print("[bench] parity check on sampled outputs", file=sys.stderr, flush=True)
+        pairs = [(i % S, (7 * i) % Hq) for i in range(0, S, max(1, S // 16))]
+        worst = parity_check(sets[0], outs[0], pairs)
+
+    for k in range(args.warmup):
+        step(sets[k % nsets], outs[k % nsets])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(K):
+        s = sets[k % nsets]
+        ev[k][0].record(stream)
+        pkv.paged_kv_write(s.k_new, s.v_new, s.k_cache, s.v_cache, s.slot_mapping)
+        ev[k][1].record(stream)
+        pkv.paged_attn_decode(outs[k % nsets], s.q, s.k_cache, s.v_cache, s.block_tables,
+                              s.context_lens, s.block_size, s.scale, max_context_len=maxL,
+                              workspace=workspace)
+        ev[k][2].record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+
+    ms_step = e0.elapsed_time(e1) / K
+    write_us = sum(e[0].elapsed_time(e[1]) for e in ev) / K * 1e3
+    decode_us = sum(e[1].elapsed_time(e[2]) for e in ev) / K * 1e3
+    decode_sorted = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in ev)
+
+    # warm (single set, back to back) decode time, for context
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    warm[0].record(stream)
+    for _ in range(20):
+        pkv.paged_attn_decode(outs[0], base.q, base.k_cache, base.v_cache, base.block_tables,
+                              base.context_lens, base.block_size, base.scale,
+                              max_context_len=maxL, workspace=workspace)
+    warm[1].record(stream)
+    torch.cuda.synchronize()
+    warm_us = warm[0].elapsed_time(warm[1]) / 20 * 1e3
+
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = kv_bytes / (decode_us * 1e-6) / 1e9
+    traffic = traffic_for(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": base.dtype,
+        "data": "synthetic (seeded N(0,1) values, shuffled block tables; no dataset)",
+        "config": {"workload": base.name, "num_seqs": S, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": base.block_size,
+                   "context_tokens": int(base.lens.sum()), "max_context_len": maxL,
+                   "kv_read_bytes_per_step": kv_bytes, "input_sets": nsets},
+        "query_tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_us": round(decode_us, 3),
+        "decode_us_p10_p90": [round(decode_sorted[len(decode_sorted) // 10], 3),
+                              round(decode_sorted[(9 * len(decode_sorted)) // 10], 3)],
+        "kv_write_us": round(write_us, 3),
+        "warm_decode_us": round(warm_us, 3),
+        "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "kernel": "paged_attn_decode (partition + merge kernels)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "parity_worst_normwise": worst,
+        "kernel_source": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(base, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,51 @@
+// KV append: copy each new token's K/V rows into its slot of the paged cache.
+//
+// "PagedAttention核心思想" section 2.4.2: a generated token is stored in the
+// next free slot of its sequence's last block (a new block is taken only when
+// that one is full); the slot is physical_block * block_size + offset.
+//
+// One thread moves one 16-byte chunk of K and the matching chunk of V.  Rows
+// of a (token, head) are head_dim * elem_bytes contiguous bytes on both sides,
+// so consecutive threads read and write consecutive 16-byte chunks.  The copy
+// is a bit copy: no conversion, NaN payloads and signed zeros survive.
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a, int chunks_per_row) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_token = (int64_t)a.num_kv_heads * chunks_per_row;
+    if (idx >= a.num_tokens * per_token) return;
+    const int64_t n = idx / per_token;
+    const int32_t rem = (int32_t)(idx - n * per_token);
+    const int32_t h = rem / chunks_per_row;
+    const int32_t c = rem - h * chunks_per_row;
+    const int64_t slot = a.slot_mapping[n];
+    if (slot < 0) return;
+    const int64_t blk = slot / a.block_size;
+    const int64_t off = slot - blk * a.block_size;
+    const int64_t row_bytes = (int64_t)a.head_dim * a.elem_bytes;
+    const int64_t dst = ((blk * a.num_kv_heads + h) * a.block_size + off) * row_bytes + (int64_t)c * 16;
+    const int64_t src_k = n * a.k_token_stride * a.elem_bytes + h * row_bytes + (int64_t)c * 16;
+    const int64_t src_v = n * a.v_token_stride * a.elem_bytes + h * row_bytes + (int64_t)c * 16;
+    const u32x4 kx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.k) + src_k);
+    const u32x4 vx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.v) + src_v);
+    *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_cache) + dst) = kx;
+    *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_cache) + dst) = vx;
+}
+
+}  // namespace
+
+hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t stream) {
+    const int chunks_per_row = a.head_dim * a.elem_bytes / 16;
+    const int64_t total = a.num_tokens * a.num_kv_heads * chunks_per_row;
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = (total + 255) / 256;
+    kv_write_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(a, chunks_per_row);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

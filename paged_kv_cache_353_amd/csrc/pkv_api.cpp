@@ -1,0 +1,142 @@
+// C ABI of libpkv.so: host-side argument checks, work planning and launches.
+// Every check here runs on the host before anything is queued; nothing reads
+// device memory or synchronises.
+#include "pkv.h"
+
+#include <cmath>
+
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+int elem_bytes(int32_t dtype) {
+    switch (dtype) {
+        case PKV_F32: return 4;
+        case PKV_F16: return 2;
+        case PKV_BF16: return 2;
+        default: return 0;
+    }
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_status_string(int status) {
+    switch (status) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_NULL: return "a required pointer is NULL";
+        case PKV_ERR_SHAPE: return "a size is out of range or sizes disagree";
+        case PKV_ERR_DTYPE: return "unknown dtype code";
+        case PKV_ERR_UNSUPPORTED: return "no kernel is built for this head_dim / block_size / head group";
+        case PKV_ERR_WORKSPACE: return "workspace missing or smaller than paged_attn_decode_workspace_size()";
+        case PKV_ERR_ALIGN: return "a pointer or token stride is not 16-byte aligned";
+        case PKV_ERR_HIP: return "the HIP runtime reported an error at launch";
+        default: return "unknown status";
+    }
+}
+
+int pkv_version(void) { return kVersion; }
+
+int paged_kv_write(const void *k, const void *v, void *k_cache, void *v_cache,
+                   const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                   int64_t k_token_stride, int64_t v_token_stride, int32_t dtype,
+                   hipStream_t stream) {
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return PKV_ERR_DTYPE;
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return PKV_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (k_token_stride < row || v_token_stride < row) return PKV_ERR_SHAPE;
+    if (num_tokens == 0) return PKV_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (k_token_stride * eb) % 16 != 0 || (v_token_stride * eb) % 16 != 0)
+        return PKV_ERR_ALIGN;
+    if (num_tokens > ((int64_t)1 << 40) / row) return PKV_ERR_SHAPE;
+    pkv::KvWriteArgs a{};
+    a.k = k;
+    a.v = v;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.k_token_stride = k_token_stride;
+    a.v_token_stride = v_token_stride;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.elem_bytes = eb;
+    return pkv::launch_kv_write(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_context_len) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_context_len < 0)
+        return 0;
+    return pkv::plan_decode(num_seqs, num_q_heads, head_dim, max_context_len).workspace_bytes;
+}
+
+int paged_attn_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                      int64_t num_blocks, int32_t max_context_len, float scale,
+                      int32_t dtype, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
+        return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return PKV_ERR_SHAPE;
+    if (num_seqs > 65535 || num_kv_heads > 65535) return PKV_ERR_SHAPE;
+    if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+    const int32_t group = num_q_heads / num_kv_heads;
+    if (!pkv::decode_supported(dtype, head_dim, group)) return PKV_ERR_UNSUPPORTED;
+    if (block_size % pkv::kSubTile != 0 || block_size > 256) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_ALIGN;
+    const pkv::DecodePlan plan = pkv::plan_decode(num_seqs, num_q_heads, head_dim, max_context_len);
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes) return PKV_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
+    }
+    pkv::DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.ws_acc = plan.workspace_bytes
+                   ? reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_acc_offset)
+                   : nullptr;
+    a.ws_ml = plan.workspace_bytes
+                  ? reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_ml_offset)
+                  : nullptr;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.part_tokens = plan.part_tokens;
+    a.max_parts = plan.max_parts;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    return pkv::launch_attn_decode(dtype, head_dim, group, a, plan, stream) == hipSuccess
+               ? PKV_OK
+               : PKV_ERR_HIP;
+}
+
+}  // extern "C"

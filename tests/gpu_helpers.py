@@ -1,0 +1,81 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+binding, run the oracle on host copies of the same inputs, compare."""
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_353_amd as pkv
+from paged_kv_cache_353_amd.workloads import DecodeInputs, to_numpy_bits
+
+# Tolerances (see the design notes): fp32 output vs the fp64 oracle, and
+# fp16/bf16 output with fp32 accumulation; each has an elementwise and a
+# per-(sequence, head) normwise bound.
+TOL = {
+    "f32": dict(atol=1e-6, rtol=1e-5, norm=1e-5),
+    "f16": dict(atol=2e-3, rtol=1e-2, norm=1e-2),
+    "bf16": dict(atol=2e-3, rtol=1e-2, norm=1e-2),
+}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def host_inputs(inp: DecodeInputs):
+    """Stored bits of every input, copied to host numpy arrays."""
+    return dict(q=to_numpy_bits(inp.q), k_cache=to_numpy_bits(inp.k_cache),
+                v_cache=to_numpy_bits(inp.v_cache), k_new=to_numpy_bits(inp.k_new),
+                v_new=to_numpy_bits(inp.v_new),
+                block_tables=inp.block_tables.cpu().numpy(),
+                context_lens=inp.context_lens.cpu().numpy(),
+                slot_mapping=inp.slot_mapping.cpu().numpy())
+
+
+def oracle_step(h, inp: DecodeInputs, pairs=None, write=True):
+    """Oracle decode step: append the new token, then attend (float64)."""
+    kc, vc = h["k_cache"], h["v_cache"]
+    if write:
+        kc, vc = oracle.paged_kv_write(h["k_new"], h["v_new"], kc, vc, h["slot_mapping"])
+    return oracle.paged_attn_decode(h["q"], kc, vc, h["block_tables"], h["context_lens"],
+                                    inp.block_size, inp.scale, inp.dtype, pairs=pairs)
+
+
+def gpu_step(inp: DecodeInputs, write=True, max_context_len=None, out=None):
+    """HIP path: paged_kv_write of the new token, then paged_attn_decode."""
+    if write:
+        pkv.paged_kv_write(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, inp.slot_mapping)
+    if out is None:
+        out = torch.empty_like(inp.q)
+    if max_context_len is None:
+        max_context_len = inp.max_context_len
+    pkv.paged_attn_decode(out, inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                          inp.context_lens, inp.block_size, inp.scale,
+                          max_context_len=max_context_len)
+    torch.cuda.synchronize()
+    return out
+
+
+def assert_close(got: torch.Tensor, want: np.ndarray, dtype: str, pairs=None, what=""):
+    """Elementwise |d| <= atol + rtol |ref| and normwise ||d|| <= norm ||ref||
+    per (sequence, head), over all outputs or the sampled pairs."""
+    tol = TOL[dtype]
+    g = got.detach().float().cpu().numpy().astype(np.float64)
+    if pairs is None:
+        pairs = [(i, h) for i in range(g.shape[0]) for h in range(g.shape[1])]
+    worst = 0.0
+    for i, h in pairs:
+        a, b = g[i, h], want[i, h]
+        assert np.all(np.isfinite(a)), f"{what}: non-finite output at seq {i} head {h}"
+        d = np.abs(a - b)
+        bad = d > tol["atol"] + tol["rtol"] * np.abs(b)
+        assert not bad.any(), (f"{what}: seq {i} head {h}: {int(bad.sum())} elements out of "
+                               f"tolerance, max |d| {d.max():.3e}")
+        nb = np.linalg.norm(b)
+        rel = np.linalg.norm(a - b) / nb if nb > 0 else np.linalg.norm(a - b)
+        assert rel <= tol["norm"], f"{what}: seq {i} head {h}: normwise error {rel:.3e}"
+        worst = max(worst, rel)
+    return worst

@@ -1,0 +1,128 @@
+"""C ABI checks that need no GPU: the library loads, exports what include/pkv.h
+declares, and rejects invalid arguments on the host before launching anything."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_353_amd as pkv
+from paged_kv_cache_353_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+PKV_OK, PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_DTYPE, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, \
+    PKV_ERR_ALIGN, PKV_ERR_HIP = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.library_path()):
+        pytest.fail("libpkv.so is not built: run __graft_entry__.build() first")
+    return pkv.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("paged_kv_write", "paged_attn_decode", "paged_attn_decode_workspace_size",
+              "pkv_status_string", "pkv_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for n in declared_functions():
+        assert n in exported, f"{n} declared in pkv.h but not exported"
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.pkv_status_string(s)
+    assert lib.pkv_status_string(99) == b"unknown status"
+    assert lib.pkv_version() >= 100
+
+
+def test_workspace_size_rules(lib):
+    f = pkv.paged_attn_decode_workspace_size
+    assert f(64, 32, 8, 128, 16, 256) == 0            # one partition: no workspace
+    small = f(64, 32, 8, 128, 16, 2048)
+    assert small >= 64 * 32 * 8 * (128 + 2) * 4
+    assert f(4, 32, 8, 128, 16, 1 << 20) > 0
+    assert f(-1, 32, 8, 128, 16, 100) == 0
+
+
+def _decode(lib, **kw):
+    args = dict(out=1 << 12, q=1 << 12, k=1 << 12, v=1 << 12, bt=1 << 12, cl=1 << 12,
+                S=4, Hq=32, Hkv=8, D=128, bs=16, mb=16, nb=64, maxL=256, scale=0.1,
+                dtype=2, ws=None, wsb=0)
+    args.update(kw)
+    a = args
+    return lib.paged_attn_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"],
+                                 a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"],
+                                 a["maxL"], a["scale"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_decode_rejects_bad_arguments_on_host(lib):
+    # These all fail host checks, so no (fake) pointer is ever dereferenced.
+    assert _decode(lib, out=None) == PKV_ERR_NULL
+    assert _decode(lib, dtype=7) == PKV_ERR_DTYPE
+    assert _decode(lib, D=96) == PKV_ERR_UNSUPPORTED
+    assert _decode(lib, Hq=24, Hkv=8) == PKV_ERR_UNSUPPORTED     # group 3
+    assert _decode(lib, Hq=30, Hkv=8) == PKV_ERR_SHAPE           # not a multiple
+    assert _decode(lib, bs=8, mb=32) == PKV_ERR_UNSUPPORTED
+    assert _decode(lib, bs=24, mb=16) == PKV_ERR_UNSUPPORTED
+    assert _decode(lib, mb=8, maxL=256) == PKV_ERR_SHAPE         # table too short
+    assert _decode(lib, S=-1) == PKV_ERR_SHAPE
+    assert _decode(lib, S=70000) == PKV_ERR_SHAPE
+    assert _decode(lib, scale=float("nan")) == PKV_ERR_SHAPE
+    assert _decode(lib, q=(1 << 12) + 2) == PKV_ERR_ALIGN
+    assert _decode(lib, maxL=2048, mb=128) == PKV_ERR_WORKSPACE  # needs a workspace
+    assert _decode(lib, maxL=2048, mb=128, ws=1 << 12, wsb=16) == PKV_ERR_WORKSPACE
+    assert _decode(lib, S=0) == PKV_OK                           # nothing to do
+
+
+def _write(lib, **kw):
+    a = dict(k=1 << 12, v=1 << 12, kc=1 << 12, vc=1 << 12, sm=1 << 12, N=4, Hkv=8, D=128,
+             bs=16, nb=64, ks=1024, vs=1024, dtype=2)
+    a.update(kw)
+    return lib.paged_kv_write(a["k"], a["v"], a["kc"], a["vc"], a["sm"], a["N"], a["Hkv"],
+                              a["D"], a["bs"], a["nb"], a["ks"], a["vs"], a["dtype"], None)
+
+
+def test_write_rejects_bad_arguments_on_host(lib):
+    assert _write(lib, N=0) == PKV_OK
+    assert _write(lib, k=None) == PKV_ERR_NULL
+    assert _write(lib, dtype=5) == PKV_ERR_DTYPE
+    assert _write(lib, D=80) == PKV_ERR_UNSUPPORTED
+    assert _write(lib, ks=100) == PKV_ERR_SHAPE
+    assert _write(lib, ks=1028) == PKV_ERR_ALIGN
+    assert _write(lib, kc=(1 << 12) + 4) == PKV_ERR_ALIGN
+    assert _write(lib, N=-3) == PKV_ERR_SHAPE
+    assert _write(lib, bs=0) == PKV_ERR_SHAPE
+
+
+def test_python_binding_validates_before_the_library():
+    import torch
+    q = torch.zeros(2, 4, 64)
+    kc = torch.zeros(4, 2, 16, 64)
+    bt = torch.zeros(2, 2, dtype=torch.int32)
+    cl = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pkv.paged_attn_decode(q, q, kc, kc, bt, cl, block_size=32, scale=1.0)
+    with pytest.raises(TypeError):
+        pkv.paged_attn_decode(q, q, kc, kc, bt.long(), cl, block_size=16, scale=1.0)
+    with pytest.raises(ValueError):
+        pkv.paged_kv_write(q, q, kc, kc, torch.zeros(2, dtype=torch.int32))
