@@ -76,8 +76,9 @@ def test_strided_token_rows():
 def test_special_bit_patterns_survive():
     say("case: kv write keeps NaN payloads and signed zeros")
     H, D = 2, 64
-    bits = torch.tensor([0x7FC1, 0x8000, 0xFF80, 0x0001, 0x7F81, 0xFFFF] * (H * D // 6 + 1),
-                        dtype=torch.int16)[: H * D].view(1, H, D)
+    pattern = np.array([0x7FC1, 0x8000, 0xFF80, 0x0001, 0x7F81, 0xFFFF] * (H * D // 6 + 1),
+                       dtype=np.uint16)[: H * D]
+    bits = torch.from_numpy(pattern.view(np.int16).copy()).view(1, H, D)
     k = bits.view(torch.bfloat16).to(DEV)
     v = k.clone()
     kc = torch.zeros((4, H, 16, D), dtype=torch.bfloat16, device=DEV)
