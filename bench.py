@@ -178,7 +178,7 @@ def main() -> int:
     S, Hq, Hkv, D = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_dim
     maxL = base.max_context_len
     ws_bytes = pkv.paged_attn_decode_workspace_size(S, Hq, Hkv, D, base.block_size, maxL)
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    workspace = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(s.q) for s in sets]
     kv_bytes = base.kv_read_bytes()
     stream = torch.cuda.current_stream()

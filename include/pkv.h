@@ -20,7 +20,8 @@
  *   slot_mapping      int64 [num_tokens]; slot = physical_block*block_size + offset
  *
  * Ownership: every pointer argument is device memory owned by the caller.  The
- * library allocates nothing, keeps no mutable global state and is reentrant; all
+ * library allocates nothing and is reentrant; its only global state is a cache
+ * of the decode kernel's occupancy per configuration, filled on first use.  All
  * work is queued asynchronously on `stream` (NULL = the null stream).  Outputs
  * are `out` and the caches; `out` must not alias q or the caches, and k/v must
  * not alias the caches.
@@ -92,11 +93,16 @@ int paged_kv_write(const void *k, const void *v, void *k_cache, void *v_cache,
                    int32_t dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace paged_attn_decode needs for these sizes (0 when a
- * single pass suffices).  Long contexts are split into partitions whose
- * partial results (running max, exp-sum, un-normalised output; fp32) are kept
- * here and merged by a second kernel.  Returns 0 for invalid sizes too; the
- * decode call reports those.
+ * Bytes of device workspace paged_attn_decode needs for these sizes (0 for
+ * invalid sizes; the decode call reports those).  The work of a batch is cut
+ * into equal pieces, one per wave the GPU runs at once; a (sequence, KV head)
+ * pair whose context is split between waves leaves one partial result per
+ * piece here (running max, exp-sum and un-normalised output, fp32), merged by
+ * the last wave to finish, which it finds through a per-pair arrival counter.
+ * The counters occupy the first 4 MiB of every workspace (2^20 of them, so
+ * num_seqs * num_kv_heads <= 2^20); partial results follow.  The size depends
+ * on num_seqs, num_kv_heads, the group size and head_dim; block_size and
+ * max_context_len are accepted for symmetry with the decode call.
  */
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
@@ -120,8 +126,18 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *   num_q_heads % num_kv_heads == 0 and the group size is 1, 2, 4 or 8
  *   head_dim 64 or 128; block_size a multiple of 16 up to 256
  *   max_blocks_per_seq*block_size >= max_context_len
- *   workspace: >= paged_attn_decode_workspace_size(...) bytes of device memory
- *              (may be NULL when that size is 0); contents need not be initialised
+ *   num_seqs * num_kv_heads <= 2^20 and
+ *   num_seqs * num_kv_heads * ceil(max_context_len / 16) < 2^31
+ *   workspace: >= paged_attn_decode_workspace_size(...) bytes of device memory,
+ *              256-byte aligned, zero-filled once before its first use (at
+ *              least its first 4 MiB).  Every call returns the counters to zero
+ *              (the rest needs no initialisation), so one workspace serves any
+ *              number of later calls, of any shape it is large enough for, on
+ *              the same stream; calls that may run at the same time need
+ *              separate workspaces.
+ * Results depend only on the logical contents and the sizes (and on the GPU's
+ * compute-unit count, which fixes how work is split): they are bitwise
+ * reproducible and do not change when blocks are relabelled or resized.
  */
 int paged_attn_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, const int32_t *context_lens,

@@ -132,9 +132,14 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     [num_blocks, num_kv_heads, block_size, head_dim]; ``block_tables`` int32
     [num_seqs, max_blocks_per_seq]; ``context_lens`` int32 [num_seqs].
     ``max_context_len`` defaults to ``max_blocks_per_seq * block_size`` (an
-    upper bound that needs no device read); a tighter value shrinks the
-    launch.  ``workspace`` (uint8, on the device) is allocated through torch
-    when not given.  Returns ``out``.
+    upper bound that needs no device read); context lengths are clamped to it.
+    ``workspace`` (uint8, on the device, at least
+    ``paged_attn_decode_workspace_size(...)`` bytes) holds partial results and
+    per-(sequence, KV head) arrival counters.  A caller-provided workspace must
+    be zero-filled once before its first use; every call returns the counters
+    to zero, so it can be reused by later calls on the same stream (not by
+    calls that run concurrently).  When not given, a zeroed one is allocated through
+    torch.  Returns ``out``.
     """
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
@@ -159,7 +164,7 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     lib = load_library()
     need = int(lib.paged_attn_decode_workspace_size(S, hq, hkv, d, bs, int(max_context_len)))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
         _check(lib.paged_attn_decode(
             out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),

@@ -7,32 +7,45 @@
 // the sequence, look its physical id up in the table, score the query against
 // the block's keys, fold the scores into a running (max, exp-sum) softmax and
 // accumulate the probability-weighted values; tokens past the sequence end in
-// the last block are masked out (never loaded, score -inf).  Long sequences are
-// cut into partitions whose partial results are merged by a second kernel (the
+// the last block are masked out (never loaded, score -inf).  Long sequences
+// are cut into pieces whose partial results are merged afterwards (the
 // partitioned "V2" scheme the CSDN answer mentions).
 //
-// Mapping to CDNA4:
-//  * Workgroup = (partition, kv head, sequence), `NW` wave64s.  All G = Hq/Hkv
-//    query heads that share the KV head are served by one load of each K/V
-//    tile (GQA grouping).
-//  * A wave scores 16 tokens at a time.  The (block, kv head) tile of 16 rows
-//    is contiguous in HBM; each lane loads 16-byte chunks with raw buffer
-//    loads whose descriptor spans only the valid rows, so tail rows of the
-//    last block are never fetched (the hardware returns 0 past num_records).
-//    Each wave load instruction reads 1 KiB of consecutive bytes.
-//  * q.k partials use v_dot2 (bf16/fp16) or FMA (fp32) on the lane's chunk,
-//    then a lane reduce-scatter over the R lanes of a row through DPP
-//    (mirror / half-mirror / quad permutes), leaving every (token, head) score
-//    fully summed in one lane.
-//  * Softmax bookkeeping runs in a "one score per lane" layout (head = lane %
-//    G); probabilities go through a 256-byte LDS slot per wave to the lanes
-//    that hold the matching V chunks; acc[G][8] fp32 per lane.
-//  * K/V tiles of the next sub-tile are loaded before the current one is
-//    consumed (two register buffers), keeping ~16 KiB in flight per wave.
-//  * The summation order depends only on logical token positions, so results
-//    are bitwise reproducible and independent of where blocks live physically.
+// Work split (one launch).  A unit is one (sequence, KV head) pair; its work
+// is ceil(L/16) sub-tiles of 16 tokens.  All sub-tiles of all units, in
+// (sequence, KV head, position) order, are cut into W equal contiguous ranges,
+// one per wave, W being what the GPU holds at once.  Every wave therefore
+// streams the same number of bytes whatever the length mix, with no empty
+// workgroups and no tail of short partitions.  A unit that lies wholly inside
+// one wave's range is finished by that wave; a unit shared by k waves gets k
+// partial results (max, exp-sum, un-normalised output) in the workspace, and
+// the wave that arrives last at the unit's counter merges them in a fixed
+// order and writes the output.  The counter is reset to zero by that wave, so
+// the workspace is left as it was found.
+//
+// One wave, one sub-tile (16 tokens of one KV head, the G query heads that
+// share it):
+//  * K and V rows come in with 16-byte raw buffer loads whose descriptor spans
+//    only the sub-tile's valid rows: tail rows of the last block read as zero
+//    and are never fetched.  The next sub-tile's loads are issued before the
+//    current one is consumed.
+//  * q.K is one 16x16 MFMA product per 32 (bf16/fp16) or 4 (fp32) dims: the
+//    16 tokens are the rows, the query heads the columns (up to 16, so any
+//    group size fits).  Lane (r, j) receives the scores of tokens 4r..4r+3 of
+//    the sub-tile for head j.
+//  * Softmax runs as four interleaved streams, one per row group r (tokens
+//    4r..4r+3 of every sub-tile), each with its own running max and exp-sum,
+//    so a sub-tile needs no exchange between row groups.  The four streams are
+//    combined once, when the wave leaves the unit.
+//  * The lanes of row group r also hold V rows 4r..4r+3; probabilities and
+//    rescale factors reach them by DPP row broadcast, and acc += p V runs on
+//    the VALU in fp32.
+//  * The summation order depends only on logical token positions and on the
+//    sizes of the problem, so results are bitwise reproducible and independent
+//    of where the blocks live physically or how large the blocks are.
 #include "pkv_internal.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace pkv {
@@ -42,19 +55,17 @@ constexpr int kWave = 64;
 constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 buffer descriptor word 3 (32-bit data)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-// Block Table and length reads go through the constant address space so they
-// become scalar loads: a vector load here would make the compiler wait for
-// every tile load already in flight (vmcnt is in order) and would turn the
-// buffer descriptor into a per-lane value.
-typedef const int32_t __attribute__((address_space(4))) *const_i32_ptr;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// Block Table and length reads go through the constant address space so they
+// become scalar loads (their addresses are wave-uniform).
+typedef const int32_t __attribute__((address_space(4))) *const_i32_ptr;
 
 struct F32 { static constexpr int kBytes = 4; };
 struct F16 { static constexpr int kBytes = 2; };
 struct BF16 { static constexpr int kBytes = 2; };
-
-constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
@@ -69,91 +80,68 @@ __device__ __forceinline__ void static_for(F &&f) {
 // (it reads element 0 whatever the index).
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
-__device__ __forceinline__ bf16x2 as_bf2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
-// ------------------------------------------------------------------ lane exchange
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kRowRor4 = 0x124;
-constexpr int kRowRor8 = 0x128;
-constexpr int kRowMirror = 0x140;   // lane c <-> 15-c within 16
-constexpr int kRowHalfMirror = 0x141;  // lane c <-> 7-c within 8
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kNegInf = -__builtin_inff();
 
-__device__ __forceinline__ float swap16(float x) {  // lane ^ 16 (within 32)
+// ------------------------------------------------------------------ lane exchange
+// Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
+}
+// Lane n of each row broadcast to the row, taking `hi` in lanes 8..15 and
+// `lo` in lanes 0..7 (the bank mask leaves banks 0 and 1 unwritten).
+template <int N>
+__device__ __forceinline__ float row_bcast_split(float lo, float hi) {
+    const int l = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, lo), 0x150 + N, 0xF, 0xF, false);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        l, __builtin_bit_cast(int, hi), 0x150 + N, 0xF, 0xC, false));
+}
+// Lane c <-> c+8 (mod 16) inside each row (DPP row_ror:8).
+__device__ __forceinline__ float row_ror8(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor16(float x) {  // lane ^ 16
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
 }
-__device__ __forceinline__ float swap32(float x, int lane) {  // lane ^ 32
+__device__ __forceinline__ float xor32(float x, int lane) {  // lane ^ 32
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, x)));
 }
-
-// Value from a partner lane whose index differs in bit BIT (and possibly in
-// lower bits, which the callers treat as still unreduced).
-template <int BIT>
-__device__ __forceinline__ float partner(float x, int lane) {
-    if constexpr (BIT == 0) return dpp<kQuadXor1>(x);
-    else if constexpr (BIT == 1) return dpp<kQuadXor2>(x);
-    else if constexpr (BIT == 2) return dpp<kRowHalfMirror>(x);
-    else if constexpr (BIT == 3) return dpp<kRowMirror>(x);
-    else if constexpr (BIT == 4) return swap16(x);
-    else return swap32(x, lane);
+__device__ __forceinline__ int shfl_up_i(int x, int delta, int lane) {
+    const int src = lane >= delta ? lane - delta : lane;
+    const int y = __builtin_amdgcn_ds_bpermute(src << 2, x);
+    return lane >= delta ? y : 0;
 }
-
-struct OpSum { __device__ float operator()(float a, float b) const { return a + b; } };
-struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
-
-// Combine x over all lanes that agree on lane-index bits below LO.
-template <int LO, typename Op>
-__device__ __forceinline__ float allreduce_from(float x, int lane, Op op) {
-    if constexpr (LO <= 0) x = op(x, dpp<kQuadXor1>(x));
-    if constexpr (LO <= 1) x = op(x, dpp<kQuadXor2>(x));
-    if constexpr (LO <= 2) x = op(x, dpp<kRowRor4>(x));
-    if constexpr (LO <= 3) x = op(x, dpp<kRowRor8>(x));
-    if constexpr (LO <= 4) x = op(x, swap16(x));
-    if constexpr (LO <= 5) x = op(x, swap32(x, lane));
+__device__ __forceinline__ int wave_sum_i(int x, int lane) {
+    for (int d = 1; d < kWave; d <<= 1) x += __builtin_amdgcn_ds_bpermute((lane ^ d) << 2, x);
+    return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+    for (int d = 1; d < kWave; d <<= 1) x += shfl_up_i(x, d, lane);
     return x;
 }
 
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Values the compiler cannot prove wave-uniform are pinned to scalar
-// registers; a buffer descriptor built from a per-lane value would be
-// wrapped in a waterfall loop around every load.
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uniform(int64_t x) {
-    const uint64_t u = (uint64_t)x;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 // ------------------------------------------------------------------ element types
+// One MFMA step over a 16-byte chunk of K rows (A, 16 tokens) and of q (B, 16 heads).
 template <typename DT>
-__device__ __forceinline__ float dot_chunk(const u32x4 &q, const u32x4 &k) {
-    float acc = 0.f;
+__device__ __forceinline__ f32x4 mfma_chunk(const u32x4 &k, const u32x4 &q, f32x4 c) {
     if constexpr (std::is_same_v<DT, BF16>) {
-        static_for<0, 4>([&]<int i>() {
-            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(q[i]), as_bf2(k[i]), acc, false);
-        });
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                        __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
     } else if constexpr (std::is_same_v<DT, F16>) {
-        static_for<0, 4>([&]<int i>() {
-            acc = __builtin_amdgcn_fdot2(as_h2(q[i]), as_h2(k[i]), acc, false);
-        });
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                       __builtin_bit_cast(f16x8, q), c, 0, 0, 0);
     } else {
-        static_for<0, 4>([&]<int i>() { acc = __builtin_fmaf(as_f(q[i]), as_f(k[i]), acc); });
+        static_for<0, 4>([&]<int i>() {
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(k[i]), as_f(q[i]), c, 0, 0, 0);
+        });
+        return c;
     }
-    return acc;
 }
 
 template <typename DT>
@@ -174,355 +162,467 @@ __device__ __forceinline__ void chunk_to_f32(const u32x4 &v, float (&f)[16 / DT:
     }
 }
 
-// Round-to-nearest-even store of one output element.
+// Round-to-nearest-even conversion of one 16-byte chunk of output elements.
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+    const uint32_t u = as_u(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 template <typename DT>
-__device__ __forceinline__ void store_elem(void *out, int64_t idx, float x) {
+__device__ __forceinline__ u32x4 pack_chunk(const float (&f)[16 / DT::kBytes]) {
+    u32x4 r;
     if constexpr (std::is_same_v<DT, BF16>) {
-        uint32_t u = as_u(x);
-        uint16_t b;
-        if ((u & 0x7FFFFFFFu) > 0x7F800000u) {
-            b = (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-        } else {
-            u += 0x7FFFu + ((u >> 16) & 1u);
-            b = (uint16_t)(u >> 16);
-        }
-        static_cast<uint16_t *>(out)[idx] = b;
+        static_for<0, 4>([&]<int i>() { r[i] = bf16_rne(f[2 * i]) | (bf16_rne(f[2 * i + 1]) << 16); });
     } else if constexpr (std::is_same_v<DT, F16>) {
-        static_cast<_Float16 *>(out)[idx] = (_Float16)x;
+        static_for<0, 4>([&]<int i>() {
+            f16x2 h;
+            h[0] = (_Float16)f[2 * i];
+            h[1] = (_Float16)f[2 * i + 1];
+            r[i] = __builtin_bit_cast(uint32_t, h);
+        });
     } else {
-        static_cast<float *>(out)[idx] = x;
+        static_for<0, 4>([&]<int i>() { r[i] = as_u(f[i]); });
     }
+    return r;
 }
 
 __device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t r, int byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
-// ------------------------------------------------------------------ partition kernel
-template <typename DT, int D, int G, int NW>
-__global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(DecodeArgs a) {
+// Partial results pass between waves that may sit on different XCDs, whose
+// L2 caches are not coherent with each other for ordinary accesses.  They are
+// written and read with the agent-coherence cache policy (sc1), the encoding
+// of relaxed agent-scope atomic accesses, so that every access is coherent on
+// its own and no whole-cache writeback or invalidate is needed.  The writer
+// waits for its stores to complete before it bumps the arrival counter; the
+// last arriver reads only after the counter told it so.
+constexpr int kCoherentSC1 = 16;  // buffer cache-policy bit sc1
+__device__ __forceinline__ void store_coherent(float *base, int bytes, int byte_off, const f32x4 &v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufferFlags);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kCoherentSC1);
+}
+__device__ __forceinline__ f32x4 load_coherent(const float *base, int bytes, int byte_off) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, bytes, kBufferFlags);
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherentSC1));
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum): every vector
+// memory access issued so far has completed.
+__device__ __forceinline__ void wait_vmem_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Position of a wave's load or compute stage in the (sequence, KV head,
+// sub-tile) order.  Every field is wave-uniform.
+struct Cursor {
+    int seq;   // sequence
+    int kvh;   // KV head
+    int sub;   // sub-tile inside the unit
+    int n;     // sub-tiles of the unit
+    int L;     // context length of the sequence
+    int pre;   // sub-tiles of one KV head summed over the sequences before `seq`
+};
+
+// ------------------------------------------------------------------ the kernel
+// No occupancy is forced on the compiler: squeezing the 16-bit, 4-head
+// configuration to 3 waves per SIMD makes it spill, and a kernel that uses
+// scratch streams ~20% slower than the spill-free one at 2 waves per SIMD.
+template <typename DT, int D, int G>
+__global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(DecodeArgs a) {
     constexpr int EB = DT::kBytes;
     constexpr int VEC = 16 / EB;          // elements per 16-byte chunk
-    constexpr int R = D / VEC;            // lanes covering one token row
-    constexpr int LOG_R = ilog2(R);
-    constexpr int RPL = kWave / R;        // rows per wave load
-    constexpr int NI = kSubTile / RPL;    // loads per lane per sub-tile (K and V each)
-    constexpr int NP = NI * G;            // q.k partials per lane
-    constexpr int LOG_NP = ilog2(NP);
-    constexpr int RS = LOG_R < LOG_NP ? LOG_R : LOG_NP;  // reduce-scatter steps
-    constexpr int NPL = NP >> RS;         // summed scores per lane afterwards
-    constexpr int LOG_G = ilog2(G);
-    constexpr int SG = kSubTile * G;      // scores per sub-tile
-    constexpr int SPL = (SG + kWave - 1) / kWave;
-    static_assert(R >= 1 && R <= kWave && (R & (R - 1)) == 0, "row must map to a power-of-two lane count");
-    static_assert(NI >= 1 && NI * RPL == kSubTile, "sub-tile must be whole wave loads");
-    static_assert((1 << LOG_G) == G, "group must be a power of two");
-
-    __shared__ float s_lds[NW][SG];       // scores, then probabilities, of the current sub-tile
-    __shared__ float a_lds[NW][G];        // per-head rescale factor
-    __shared__ float m_lds[NW][G];
-    __shared__ float l_lds[NW][G];
-    __shared__ float acc_lds[NW][G][D];
+    constexpr int R = D * EB / 16;        // 16-byte chunks per token row
+    constexpr int NL = R / 4;             // 16-byte loads per lane per sub-tile, K and V each
+    constexpr int NCH = R >= 16 ? R / 16 : 1;  // distinct V chunks (dims) a lane accumulates
+    constexpr int ROW = D * EB;           // bytes per token row
+    static_assert(R == 8 || R == 16 || R == 32, "row must be 8, 16 or 32 chunks");
+    static_assert(G >= 1 && G <= 16, "query heads per KV head must fit the 16 MFMA columns");
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int part = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int seq = blockIdx.z;
-    const int Hq = a.num_q_heads;
-    const int P = a.part_tokens;
-    int L = ((const_i32_ptr)a.context_lens)[seq];
-    L = L < a.max_context_len ? L : a.max_context_len;
-    L = L > 0 ? L : 0;
-    const int64_t out_row0 = (int64_t)seq * Hq + (int64_t)kvh * G;  // first q head of the group
+    const int rg = lane >> 4;   // row group
+    const int c = lane & 15;    // lane inside the row
+    const int wave = uniform((int)blockIdx.x * kWavesPerGroup + (int)(threadIdx.x >> 6));
+    const int S = a.num_seqs, Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+    const int Lmax = a.max_context_len, BS = a.block_size;
+    const int W = a.num_waves;
+    const const_i32_ptr lens = (const_i32_ptr)a.context_lens;
+    auto clampL = [&](int L) { L = L < Lmax ? L : Lmax; return L > 0 ? L : 0; };
 
-    if (L == 0) {  // empty context: the output is the empty sum
-        if (part == 0)
-            for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave)
-                store_elem<DT>(a.out, out_row0 * D + idx, 0.f);
-        return;
+    // ---- empty contexts: the output is the empty sum
+    for (int i = wave; i < S; i += W) {
+        if (clampL(lens[i]) == 0) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            char *o = static_cast<char *>(a.out) + (int64_t)i * Hq * ROW;
+            for (int off = lane * 16; off < Hq * ROW; off += kWave * 16)
+                *reinterpret_cast<u32x4 *>(o + off) = z;
+        }
     }
-    const int T0 = part * P;
-    if (T0 >= L) return;
-    const int nparts = (L + P - 1) / P;
-    const int T1 = min(L, T0 + P);
-    const int nsub = (T1 - T0 + kSubTile - 1) / kSubTile;
 
-    const int g = lane / R;  // row inside one wave load
-    const int c = lane % R;  // 16-byte chunk inside the row
+    // ---- total work T (sub-tiles over all units) and this wave's range
+    int N = 0;
+    for (int base = 0; base < S; base += kWave) {
+        const int i = base + lane;
+        const int L = i < S ? clampL(a.context_lens[i]) : 0;
+        N += (L + 15) >> 4;
+    }
+    N = uniform(wave_sum_i(N, lane));
+    // sub-tile indices fit in 32 bits (the host rejects larger batches);
+    // products with a wave count are formed in 64 bits
+    const int T = N * Hkv;
+    const int Weff = T < W ? T : W;    // every wave below Weff gets >= 1 sub-tile
+    if (wave >= Weff) return;
+    const int g0 = (int)((int64_t)wave * T / Weff);
+    const int g1 = (int)((int64_t)(wave + 1) * T / Weff);
 
-    // q chunks of the G query heads that read this KV head
-    u32x4 qr[G];
+    // ---- locate g0: sequence (prefix scan of sub-tile counts), KV head, sub-tile
+    Cursor cur{};
     {
-        const char *qb = static_cast<const char *>(a.q) + (out_row0 * D) * EB + c * 16;
-        static_for<0, G>([&]<int h>() { qr[h] = *reinterpret_cast<const u32x4 *>(qb + h * D * EB); });
+        int pre = 0;
+        for (int base = 0; base < S; base += kWave) {
+            const int i = base + lane;
+            const int L = i < S ? clampL(a.context_lens[i]) : 0;
+            const int n = (L + 15) >> 4;
+            const int incl = wave_incl_scan(n, lane);
+            const uint64_t hit = __builtin_amdgcn_ballot_w64((pre + incl) * Hkv > g0);
+            if (hit) {
+                const int f = __builtin_ctzll(hit);
+                cur.seq = base + f;
+                cur.L = __builtin_amdgcn_readlane(L, f);
+                cur.n = __builtin_amdgcn_readlane(n, f);
+                cur.pre = pre + __builtin_amdgcn_readlane(incl - n, f);
+                break;
+            }
+            pre += __builtin_amdgcn_readlane(incl, kWave - 1);
+        }
+        const int rem = g0 - cur.pre * Hkv;
+        cur.kvh = rem / cur.n;
+        cur.sub = rem - cur.kvh * cur.n;
     }
+    auto advance = [&](Cursor &u) {
+        if (++u.sub < u.n) return;
+        u.sub = 0;
+        if (++u.kvh < Hkv) return;
+        u.kvh = 0;
+        u.pre += u.n;
+        do {
+            ++u.seq;
+            u.L = clampL(lens[u.seq]);
+        } while (u.L == 0);
+        u.n = (u.L + 15) >> 4;
+    };
 
-    const const_i32_ptr table = (const_i32_ptr)(a.block_tables + (int64_t)seq * a.max_blocks_per_seq);
-    const int BS = a.block_size;
-    const int64_t head_elems = (int64_t)BS * D;
-    const int64_t block_elems = (int64_t)a.num_kv_heads * head_elems;
     const char *kc = static_cast<const char *>(a.k_cache);
     const char *vc = static_cast<const char *>(a.v_cache);
+    const int64_t head_bytes = (int64_t)BS * ROW;
+    const int64_t block_bytes = (int64_t)Hkv * head_bytes;
+    const int subs_per_block = BS >> 4;
+    // per-lane byte offsets inside a sub-tile: K as MFMA rows (token = lane % 16,
+    // dims 64b + 16*(lane/16) bytes for load b); V rows 4*rg.. (see NL loads)
+    const int koff = c * ROW + 16 * rg;
+    const int voff = (4 * rg + (c / R)) * ROW + (c % R) * 16;
 
-    float m_run = -__builtin_inff();   // running max of this lane's head (lane % G)
-    float l_run = 0.f;                 // this lane's share of the exp-sum
-    float acc[G][VEC];
-    static_for<0, G>([&]<int h>() { static_for<0, VEC>([&]<int e>() { acc[h][e] = 0.f; }); });
-
-    // Issues the K and V loads of sub-tile `st`.  A sub-tile past the end of
-    // the partition gets an empty buffer range: the loads return zeros without
-    // touching memory, so the caller can issue them unconditionally (a
-    // conditional load would make the wait counters drain the prefetch).
-    auto load_tile = [&](int st, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
-        const int t0 = T0 + st * kSubTile;
-        // rows left in the partition from t0; only the first 16 are ever
-        // addressed, so the descriptor needs no upper clamp (a two-sided clamp
-        // becomes a VALU med3 whose register hazard drains the load queue)
-        int rows = T1 - t0;
-        rows = rows > 0 ? rows : 0;
-        const int tc = rows > 0 ? t0 : T0;  // keeps the table read inside the row
-        const int j = tc / BS;
-        const int row0 = tc - j * BS;
+    // Issues the K and V loads of the sub-tile at `u`; `live` false gives an
+    // empty range (loads return zeros and touch no memory), which keeps the
+    // number of loads in flight the same on every iteration.
+    auto issue = [&](const Cursor &u, bool live, u32x4 (&kr)[NL], u32x4 (&vr)[NL]) {
+        const int t0 = u.sub << 4;
+        const int j = u.sub / subs_per_block;
+        const int row0 = t0 - j * BS;
+        int rows = u.L - t0;
+        rows = rows < 16 ? rows : 16;
+        rows = live ? rows : 0;
+        const const_i32_ptr table = (const_i32_ptr)(a.block_tables + (int64_t)u.seq * a.max_blocks_per_seq);
         const int64_t phys = table[j];
-        const int64_t off = uniform((phys * block_elems + (int64_t)kvh * head_elems + (int64_t)row0 * D) * EB);
-        const int nbytes = uniform(rows * D * EB);
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kc + off), 0, nbytes, kBufferFlags);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vc + off), 0, nbytes, kBufferFlags);
-        static_for<0, NI>([&]<int i>() { kr[i] = load_chunk(rk, ((i * RPL + g) * D) * EB + c * 16); });
-        static_for<0, NI>([&]<int i>() { vr[i] = load_chunk(rv, ((i * RPL + g) * D) * EB + c * 16); });
+        const int64_t off = phys * block_bytes + (int64_t)u.kvh * head_bytes + (int64_t)row0 * ROW;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kc + off), 0, rows * ROW, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vc + off), 0, rows * ROW, kBufferFlags);
+        static_for<0, NL>([&]<int b>() { kr[b] = load_chunk(rk, koff + 64 * b); });
+        static_for<0, NL>([&]<int m>() { vr[m] = load_chunk(rv, voff + 256 * m); });
+        // keep the compute of the previous sub-tile (and its waits) after these
+        // loads, so that they are in flight while it runs
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    auto process_tile = [&](int st, const u32x4 (&kr)[NI], const u32x4 (&vr)[NI]) {
-        const int t0 = T0 + st * kSubTile;
-        const int nvalid = min(kSubTile, L - t0);
-        // ---- q.k partial sums over this lane's chunk, then reduce-scatter across the row
-        float pd[NP];
-        static_for<0, NI>([&]<int i>() {
-            static_for<0, G>([&]<int h>() { pd[i * G + h] = dot_chunk<DT>(qr[h], kr[i]); });
-        });
-        static_for<0, LOG_R>([&]<int s>() {
-            constexpr int bit = LOG_R - 1 - s;
-            if constexpr (s < RS) {
-                constexpr int half = (NP >> s) / 2;
-                const bool hi = (c >> bit) & 1;
-                static_for<0, half>([&]<int k>() {
-                    const float lo_v = pd[k], hi_v = pd[k + half];
-                    const float send = hi ? lo_v : hi_v;
-                    const float keep = hi ? hi_v : lo_v;
-                    pd[k] = keep + partner<bit>(send, lane);
-                });
-            } else {
-                pd[0] = pd[0] + partner<bit>(pd[0], lane);
-            }
-        });
-        {
-            const int jbase = (c >> (LOG_R - RS)) * NPL;
-            const bool writer = (c & ((1 << (LOG_R - RS)) - 1)) == 0;
-            if (writer) {
-                static_for<0, NPL>([&]<int k>() {
-                    const int jj = jbase + k;
-                    const int tok = (jj / G) * RPL + g;
-                    s_lds[wave][tok * G + (jj % G)] = pd[k];
-                });
-            }
-        }
-        wave_sync();
-        // ---- softmax update in the one-score-per-lane layout (head = lane % G)
-        float sv[SPL];
-        float tmax = -__builtin_inff();
-        static_for<0, SPL>([&]<int u>() {
-            const int idx = lane + u * kWave;
-            const int tok = idx / G;
-            float x = -__builtin_inff();
-            if (idx < SG && tok < nvalid) x = s_lds[wave][idx] * a.scale_log2;
-            sv[u] = x;
-            tmax = fmaxf(tmax, x);
-        });
-        tmax = allreduce_from<LOG_G>(tmax, lane, OpMax{});
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = fast_exp2(m_run - m_new);
-        const bool grew = m_new > m_run;
-        m_run = m_new;
-        float psum = 0.f;
-        static_for<0, SPL>([&]<int u>() {
-            const int idx = lane + u * kWave;
-            const float p = fast_exp2(sv[u] - m_new);
-            psum += p;
-            if (idx < SG) s_lds[wave][idx] = p;
-        });
-        l_run = l_run * alpha + psum;
-        if (__builtin_amdgcn_ballot_w64(grew) != 0) {
-            if (lane < G) a_lds[wave][lane] = alpha;
-            wave_sync();
-            static_for<0, G>([&]<int h>() {
-                const float al = a_lds[wave][h];
-                static_for<0, VEC>([&]<int e>() { acc[h][e] *= al; });
-            });
-        }
-        wave_sync();
-        // ---- acc += p * V for the lane's chunk of each of its rows
-        static_for<0, NI>([&]<int i>() {
-            const int tok = i * RPL + g;
-            float pv[G];
-            static_for<0, G>([&]<int h>() { pv[h] = s_lds[wave][tok * G + h]; });
-            float vf[VEC];
-            chunk_to_f32<DT>(vr[i], vf);
-            static_for<0, G>([&]<int h>() {
-                static_for<0, VEC>([&]<int e>() { acc[h][e] = __builtin_fmaf(pv[h], vf[e], acc[h][e]); });
-            });
-        });
-        wave_sync();
-    };
+    // ---- per-unit state
+    u32x4 qr[NL];                 // B operand: head = lane % 16 (zero past G)
+    float m_run = kNegInf;        // lane (rg, j): running max of stream rg, head j (log2 units)
+    float l_run = 0.f;            // its exp-sum
+    float acc[G][NCH][VEC];       // lane (rg, c): un-normalised output of stream rg
+    int seg_first = g0;           // first sub-tile of the current segment
 
-    // ---- main loop: sub-tiles wave, wave+NW, ...; the next tile's loads are
-    // always in flight while the current one is consumed
-    {
-        u32x4 ka[NI], va[NI], kb[NI], vb[NI];
-        int st = wave;
-        load_tile(st, ka, va);
-        while (true) {
-            load_tile(st + NW, kb, vb);
-            if (st >= nsub) break;
-            process_tile(st, ka, va);
-            st += NW;
-            load_tile(st + NW, ka, va);
-            if (st >= nsub) break;
-            process_tile(st, kb, vb);
-            st += NW;
-        }
-    }
-
-    // ---- wave totals: exp-sum per head, acc summed over the rows of a load
-    const float l_tot = allreduce_from<LOG_G>(l_run, lane, OpSum{});
-    static_for<0, G>([&]<int h>() {
-        static_for<0, VEC>([&]<int e>() { acc[h][e] = allreduce_from<LOG_R>(acc[h][e], lane, OpSum{}); });
-    });
-    if (lane < G) {
-        m_lds[wave][lane] = m_run;
-        l_lds[wave][lane] = l_tot;
-    }
-    if (g == 0) {
+    auto start_unit = [&](const Cursor &u) {
+        const char *qb = static_cast<const char *>(a.q) + ((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW;
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, G * ROW, kBufferFlags);
+        const int qoff = c * ROW + 16 * rg;  // head c (out of range, so zero, for c >= G)
+        static_for<0, NL>([&]<int b>() { qr[b] = load_chunk(rq, qoff + 64 * b); });
+        // wait for q here, so that the sub-tile loop is entered with nothing
+        // but its own loads in flight and its waits stay exact
+#pragma unroll
+        for (int b = 0; b < NL; ++b) asm volatile("" ::"v"(qr[b]));
+        m_run = kNegInf;
+        l_run = 0.f;
         static_for<0, G>([&]<int h>() {
-            static_for<0, VEC>([&]<int e>() { acc_lds[wave][h][c * VEC + e] = acc[h][e]; });
+            static_for<0, NCH>([&]<int ch>() { static_for<0, VEC>([&]<int e>() { acc[h][ch][e] = 0.f; }); });
         });
-    }
-    __syncthreads();
+    };
 
-    // ---- merge the waves of this workgroup; finish or hand the partial on
-    for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
-        const int h = idx / D;
-        const int d = idx - h * D;
-        float M = -__builtin_inff();
-        static_for<0, NW>([&]<int w>() { M = fmaxf(M, m_lds[w][h]); });
-        float num = 0.f, den = 0.f;
-        static_for<0, NW>([&]<int w>() {
-            const float sc = fast_exp2(m_lds[w][h] - M);
-            num = __builtin_fmaf(sc, acc_lds[w][h][d], num);
-            den = __builtin_fmaf(sc, l_lds[w][h], den);
+    // Merges the four row-group streams of (m, l, acc); afterwards every lane
+    // holds the totals: m, l for head (lane % 16), acc for its chunks.
+    auto combine_rows = [&](float &m, float &l, float (&ac)[G][NCH][VEC], bool fold_half_rows) {
+        float M = fmaxf(m, xor16(m));
+        M = fmaxf(M, xor32(M, lane));
+        const float Mu = M == kNegInf ? 0.f : M;
+        const float sc = fast_exp2(m - Mu);
+        float Ls = l * sc;
+        Ls += xor16(Ls);
+        Ls += xor32(Ls, lane);
+        static_for<0, G>([&]<int h>() {
+            const float s = row_bcast<h>(sc);
+            static_for<0, NCH>([&]<int ch>() {
+                static_for<0, VEC>([&]<int e>() {
+                    float x = ac[h][ch][e] * s;
+                    x += xor16(x);
+                    x += xor32(x, lane);
+                    if constexpr (R == 8) {
+                        if (fold_half_rows) x += row_ror8(x);
+                    }
+                    ac[h][ch][e] = x;
+                });
+            });
         });
-        const int64_t row = out_row0 + h;
-        if (nparts == 1) {
-            store_elem<DT>(a.out, row * D + d, num / den);
-        } else {
-            const int64_t pr = row * a.max_parts + part;
-            a.ws_acc[pr * D + d] = num;
-            if (d == 0) {
-                a.ws_ml[pr * 2] = M;
-                a.ws_ml[pr * 2 + 1] = den;
+        m = M;
+        l = Ls;
+    };
+
+    // Chunk index (within a row) of accumulator chunk `ch` of this lane.
+    auto chunk_of = [&](int ch) { return R == 32 ? ch * 16 + c : (R == 8 ? (c & 7) : c); };
+    const bool chunk_writer = R == 8 ? (rg == 0 && c < 8) : rg == 0;
+
+    auto write_out = [&](const Cursor &u, const float (&ac)[G][NCH][VEC], float l) {
+        char *ob = static_cast<char *>(a.out) + ((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW;
+        static_for<0, G>([&]<int h>() {
+            const float inv = 1.f / row_bcast<h>(l);
+            static_for<0, NCH>([&]<int ch>() {
+                float f[VEC];
+                static_for<0, VEC>([&]<int e>() { f[e] = ac[h][ch][e] * inv; });
+                const u32x4 pk = pack_chunk<DT>(f);
+                if (chunk_writer) *reinterpret_cast<u32x4 *>(ob + h * ROW + chunk_of(ch) * 16) = pk;
+            });
+        });
+    };
+
+    // Leaves the unit at `u` after sub-tile `g_last`: finish it here, or hand
+    // a partial result on and merge if this wave is the last to arrive.
+    auto finish_unit = [&](const Cursor &u, int g_last) {
+        combine_rows(m_run, l_run, acc, true);
+        const int ua = Hkv * u.pre + u.kvh * u.n;  // unit's first sub-tile
+        const int ub = ua + u.n;
+        if (seg_first == ua && g_last + 1 == ub) {  // the whole unit was ours
+            write_out(u, acc, l_run);
+            return;
+        }
+        const int w_first = (int)(((int64_t)(ua + 1) * Weff - 1) / T);
+        const int w_last = (int)(((int64_t)ub * Weff - 1) / T);
+        const int k = w_last - w_first + 1;
+        const int unit = u.seq * Hkv + u.kvh;
+        // partial record of this segment: acc[G][D] then (max, exp-sum)[G]
+        constexpr int kRecAcc = G * D * 4;
+        constexpr int kRecMl = G * 2 * 4;
+        const int64_t slot = (int64_t)wave + unit;
+        float *pacc = a.ws_acc + slot * G * D;
+        float *pml = a.ws_ml + slot * G * 2;
+        static_for<0, G>([&]<int h>() {
+            static_for<0, NCH>([&]<int ch>() {
+                if (chunk_writer) {
+                    static_for<0, VEC / 4>([&]<int v4>() {
+                        const f32x4 x = {acc[h][ch][4 * v4], acc[h][ch][4 * v4 + 1], acc[h][ch][4 * v4 + 2],
+                                         acc[h][ch][4 * v4 + 3]};
+                        store_coherent(pacc, kRecAcc, (h * D + chunk_of(ch) * VEC + 4 * v4) * 4, x);
+                    });
+                }
+            });
+        });
+        if (rg == 0 && c < G) {
+            __hip_atomic_store(pml + 2 * c, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pml + 2 * c + 1, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vmem_done();
+        int old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(a.ws_cnt + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readlane(old, 0);
+        if (old != k - 1) return;
+        // last to arrive: merge the k records (this segment's included, read
+        // back) into the now free accumulators; row group rg takes records
+        // rg, rg+4, ... so the order is fixed whichever wave came last
+        float mm = kNegInf, ll = 0.f;
+        static_for<0, G>([&]<int h>() {
+            static_for<0, NCH>([&]<int ch>() { static_for<0, VEC>([&]<int e>() { acc[h][ch][e] = 0.f; }); });
+        });
+        for (int r = rg; r < k; r += 4) {
+            const int64_t s2 = (int64_t)(w_first + r) + unit;
+            const float *racc = a.ws_acc + s2 * G * D;
+            const float *rml = a.ws_ml + s2 * G * 2;
+            float Mr = kNegInf, Lr = 0.f;
+            if (c < G) {
+                Mr = __hip_atomic_load(rml + 2 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                Lr = __hip_atomic_load(rml + 2 * c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+            const float mn = fmaxf(mm, Mr);
+            const float mu = mn == kNegInf ? 0.f : mn;
+            const float al = fast_exp2(mm - mu);
+            const float be = fast_exp2(Mr - mu);
+            ll = ll * al + Lr * be;
+            mm = mn;
+            static_for<0, G>([&]<int h>() {
+                const float alh = row_bcast<h>(al);
+                const float beh = row_bcast<h>(be);
+                static_for<0, NCH>([&]<int ch>() {
+                    static_for<0, VEC / 4>([&]<int v4>() {
+                        const f32x4 x = load_coherent(racc, kRecAcc, (h * D + chunk_of(ch) * VEC + 4 * v4) * 4);
+                        static_for<0, 4>([&]<int e>() {
+                            acc[h][ch][4 * v4 + e] = acc[h][ch][4 * v4 + e] * alh + x[e] * beh;
+                        });
+                    });
+                });
+            });
+        }
+        combine_rows(mm, ll, acc, false);
+        write_out(u, acc, ll);
+        if (lane == 0) __hip_atomic_store(a.ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
+    // One sub-tile: scores on MFMA, four-stream online softmax, acc += p V.
+    auto process = [&](const Cursor &u, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        static_for<0, NL>([&]<int b>() { s = mfma_chunk<DT>(kr[b], qr[b], s); });
+        const int nvalid = u.L - (u.sub << 4);  // >= 1
+        float sv[4];
+        float tmax = kNegInf;
+        static_for<0, 4>([&]<int r>() {
+            sv[r] = (4 * rg + r < nvalid) ? s[r] * a.scale_log2 : kNegInf;
+            tmax = fmaxf(tmax, sv[r]);
+        });
+        const float m_new = fmaxf(m_run, tmax);
+        const float mu = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - mu);
+        float p[4];
+        static_for<0, 4>([&]<int r>() { p[r] = fast_exp2(sv[r] - mu); });
+        l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        m_run = m_new;
+        if (__builtin_amdgcn_ballot_w64(c < G && alpha != 1.f) != 0) {
+            static_for<0, G>([&]<int h>() {
+                const float ah = row_bcast<h>(alpha);
+                static_for<0, NCH>([&]<int ch>() { static_for<0, VEC>([&]<int e>() { acc[h][ch][e] *= ah; }); });
+            });
+        }
+        // V slot mm of this lane holds token 4*rg + mm (16 chunks a row),
+        // mm/2 (32 chunks) or 2*mm + (c >= 8) (8 chunks)
+        static_for<0, NL>([&]<int mm>() {
+            float vf[VEC];
+            chunk_to_f32<DT>(vr[mm], vf);
+            constexpr int ch = NCH == 2 ? (mm & 1) : 0;
+            static_for<0, G>([&]<int h>() {
+                float ph;
+                if constexpr (R == 16) ph = row_bcast<h>(p[mm]);
+                else if constexpr (R == 32) ph = row_bcast<h>(p[mm >> 1]);
+                else ph = row_bcast_split<h>(p[2 * mm], p[2 * mm + 1]);
+                static_for<0, VEC>([&]<int e>() { acc[h][ch][e] = __builtin_fmaf(ph, vf[e], acc[h][ch][e]); });
+            });
+        });
+    };
+
+    // ---- main loop over [g0, g1): one outer iteration per segment (the part
+    // of a unit inside this range).  The inner loop keeps two sub-tiles in
+    // flight and issues loads unconditionally (empty ranges past the end), so
+    // its waits only ever cover the sub-tile being consumed; the first
+    // sub-tile of the next segment is already in flight when a segment ends.
+    u32x4 ka[NL], va[NL], kb[NL], vb[NL];
+    Cursor cp = cur;   // sub-tile g, held in ka/va
+    Cursor cl = cur;   // most recently issued sub-tile
+    issue(cl, true, ka, va);
+    int g = g0;
+    while (true) {
+        start_unit(cp);
+        seg_first = g;
+        bool next_in_b;
+        while (true) {
+            bool more = g + 1 < g1;
+            if (more) advance(cl);
+            issue(cl, more, kb, vb);
+            process(cp, ka, va);
+            if (cp.sub + 1 == cp.n || !more) { next_in_b = true; break; }
+            cp = cl;
+            ++g;
+            more = g + 1 < g1;
+            if (more) advance(cl);
+            issue(cl, more, ka, va);
+            process(cp, kb, vb);
+            if (cp.sub + 1 == cp.n || !more) { next_in_b = false; break; }
+            cp = cl;
+            ++g;
+        }
+        finish_unit(cp, g);
+        if (g + 1 >= g1) break;
+        ++g;
+        cp = cl;
+        if (next_in_b) {
+            static_for<0, NL>([&]<int b>() { ka[b] = kb[b]; va[b] = vb[b]; });
         }
     }
 }
-
-// ------------------------------------------------------------------ merge kernel
-// Per (sequence, q head): out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-constexpr int kReduceThreads = 256;
-
-__device__ float block_reduce(float x, float *scratch, bool is_max) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    x = is_max ? allreduce_from<0>(x, lane, OpMax{}) : allreduce_from<0>(x, lane, OpSum{});
-    if (lane == 0) scratch[wave] = x;
-    __syncthreads();
-    float r = scratch[0];
-    for (int w = 1; w < kReduceThreads / 64; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
-    __syncthreads();
-    return r;
-}
-
-template <typename DT, int D>
-__global__ __launch_bounds__(kReduceThreads) void attn_merge_kernel(DecodeArgs a) {
-    constexpr int NS = kReduceThreads / D;  // partition slices summed in parallel
-    __shared__ float w_lds[kMaxParts];
-    __shared__ float part_lds[kReduceThreads];
-    __shared__ float scratch[kReduceThreads / 64];
-    const int h = blockIdx.x;
-    const int seq = blockIdx.y;
-    const int P = a.part_tokens;
-    int L = a.context_lens[seq];
-    L = L < a.max_context_len ? L : a.max_context_len;
-    L = L > 0 ? L : 0;
-    const int n = (L + P - 1) / P;
-    if (n <= 1) return;  // written directly by the partition kernel
-    const int64_t row = (int64_t)seq * a.num_q_heads + h;
-    const float *ml = a.ws_ml + row * a.max_parts * 2;
-    const float *acc = a.ws_acc + row * a.max_parts * D;
-    const int tid = threadIdx.x;
-
-    float M = -__builtin_inff();
-    for (int p = tid; p < n; p += kReduceThreads) M = fmaxf(M, ml[2 * p]);
-    M = block_reduce(M, scratch, true);
-    float den = 0.f;
-    for (int p = tid; p < n; p += kReduceThreads) {
-        const float w = fast_exp2(ml[2 * p] - M);
-        w_lds[p] = w;
-        den = __builtin_fmaf(w, ml[2 * p + 1], den);
-    }
-    den = block_reduce(den, scratch, false);  // its barriers also publish w_lds
-
-    const int d = tid % D;
-    const int slice = tid / D;
-    float num = 0.f;
-    for (int p = slice; p < n; p += NS) num = __builtin_fmaf(w_lds[p], acc[(int64_t)p * D + d], num);
-    part_lds[tid] = num;
-    __syncthreads();
-    if (slice == 0) {
-        float s = part_lds[d];
-        for (int k = 1; k < NS; ++k) s += part_lds[k * D + d];
-        store_elem<DT>(a.out, row * D + d, s / den);
-    }
-}
-
-// ------------------------------------------------------------------ dispatch
-constexpr int kWavesPerGroup = 4;
 
 template <typename DT, int D, int G>
-hipError_t launch_typed(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream) {
-    const dim3 grid((unsigned)plan.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    attn_partition_kernel<DT, D, G, kWavesPerGroup><<<grid, dim3(kWavesPerGroup * kWave), 0, stream>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.max_parts <= 1) return e;
-    attn_merge_kernel<DT, D><<<dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(kReduceThreads), 0, stream>>>(a);
+hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.num_waves / kWavesPerGroup));
+    attn_stream_kernel<DT, D, G><<<grid, dim3(kWavesPerGroup * kWave), 0, stream>>>(a);
     return hipGetLastError();
 }
 
+template <typename DT, int D, int G>
+int waves_per_cu_typed() {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_stream_kernel<DT, D, G>,
+                                                     kWavesPerGroup * kWave, 0) != hipSuccess)
+        return 0;
+    return blocks * kWavesPerGroup;
+}
+
 template <typename DT, int D>
-hipError_t launch_group(int group, const DecodeArgs &a, const DecodePlan &plan, hipStream_t s) {
+hipError_t launch_group(int group, const DecodeArgs &a, hipStream_t s) {
     switch (group) {
-        case 1: return launch_typed<DT, D, 1>(a, plan, s);
-        case 2: return launch_typed<DT, D, 2>(a, plan, s);
-        case 4: return launch_typed<DT, D, 4>(a, plan, s);
-        case 8: return launch_typed<DT, D, 8>(a, plan, s);
+        case 1: return launch_typed<DT, D, 1>(a, s);
+        case 2: return launch_typed<DT, D, 2>(a, s);
+        case 4: return launch_typed<DT, D, 4>(a, s);
+        case 8: return launch_typed<DT, D, 8>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename DT, int D>
+int waves_group(int group) {
+    switch (group) {
+        case 1: return waves_per_cu_typed<DT, D, 1>();
+        case 2: return waves_per_cu_typed<DT, D, 2>();
+        case 4: return waves_per_cu_typed<DT, D, 4>();
+        case 8: return waves_per_cu_typed<DT, D, 8>();
+        default: return 0;
+    }
+}
+
+template <typename DT>
+hipError_t launch_dim(int head_dim, int group, const DecodeArgs &a, hipStream_t s) {
+    switch (head_dim) {
+        case 64: return launch_group<DT, 64>(group, a, s);
+        case 128: return launch_group<DT, 128>(group, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename DT>
-hipError_t launch_dim(int head_dim, int group, const DecodeArgs &a, const DecodePlan &plan, hipStream_t s) {
+int waves_dim(int head_dim, int group) {
     switch (head_dim) {
-        case 64: return launch_group<DT, 64>(group, a, plan, s);
-        case 128: return launch_group<DT, 128>(group, a, plan, s);
-        default: return hipErrorInvalidValue;
+        case 64: return waves_group<DT, 64>(group);
+        case 128: return waves_group<DT, 128>(group);
+        default: return 0;
     }
 }
 
@@ -535,34 +635,31 @@ bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group) {
     return dt && hd && gr;
 }
 
-DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                       int32_t max_context_len) {
-    DecodePlan p{};
-    p.waves = kWavesPerGroup;
-    // 256 tokens per workgroup (4 waves x 4 sub-tiles) by default; long
-    // contexts take larger partitions so that a sequence has <= 1024 of them.
-    int part = 256;
-    const int64_t need = ((int64_t)max_context_len + 1023) / 1024;
-    while (part < need) part *= 2;
-    p.part_tokens = part;
-    const int64_t parts = ((int64_t)max_context_len + part - 1) / part;
-    p.max_parts = (int32_t)(parts > 1 ? parts : 1);
-    if (p.max_parts > 1) {
-        const size_t rows = (size_t)num_seqs * (size_t)num_q_heads * (size_t)p.max_parts;
-        p.ws_acc_offset = 0;
-        const size_t acc_bytes = rows * (size_t)head_dim * sizeof(float);
-        p.ws_ml_offset = (acc_bytes + 255) & ~(size_t)255;
-        p.workspace_bytes = p.ws_ml_offset + rows * 2 * sizeof(float);
+int decode_waves_per_cu(int32_t dtype, int32_t head_dim, int32_t group) {
+    // The occupancy query is slow next to a launch, and its answer is a
+    // property of the compiled kernel: ask once per configuration (a racing
+    // first call computes the same value twice, which is harmless).
+    static std::atomic<int> cache[3][2][4];
+    const int hd = head_dim == 128 ? 1 : 0;
+    const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
+    if (dtype < 0 || dtype > 2) return 0;
+    int v = cache[dtype][hd][gi].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    switch (dtype) {
+        case 0: v = waves_dim<F32>(head_dim, group); break;
+        case 1: v = waves_dim<F16>(head_dim, group); break;
+        default: v = waves_dim<BF16>(head_dim, group); break;
     }
-    return p;
+    if (v > 0) cache[dtype][hd][gi].store(v, std::memory_order_relaxed);
+    return v;
 }
 
 hipError_t launch_attn_decode(int32_t dtype, int32_t head_dim, int32_t group,
-                              const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream) {
+                              const DecodeArgs &a, hipStream_t stream) {
     switch (dtype) {
-        case 0: return launch_dim<F32>(head_dim, group, a, plan, stream);
-        case 1: return launch_dim<F16>(head_dim, group, a, plan, stream);
-        case 2: return launch_dim<BF16>(head_dim, group, a, plan, stream);
+        case 0: return launch_dim<F32>(head_dim, group, a, stream);
+        case 1: return launch_dim<F16>(head_dim, group, a, stream);
+        case 2: return launch_dim<BF16>(head_dim, group, a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -79,10 +79,11 @@ int paged_kv_write(const void *k, const void *v, void *k_cache, void *v_cache,
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t block_size, int32_t max_context_len) {
-    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        block_size <= 0 || max_context_len < 0)
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads != 0 ||
+        (int64_t)num_seqs * num_kv_heads > pkv::kMaxUnits)
         return 0;
-    return pkv::plan_decode(num_seqs, num_q_heads, head_dim, max_context_len).workspace_bytes;
+    return pkv::decode_workspace(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim).bytes;
 }
 
 int paged_attn_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -99,19 +100,34 @@ int paged_attn_decode(void *out, const void *q, const void *k_cache, const void 
     if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
     if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return PKV_ERR_SHAPE;
     if (num_seqs > 65535 || num_kv_heads > 65535) return PKV_ERR_SHAPE;
+    if ((int64_t)num_seqs * num_kv_heads > pkv::kMaxUnits) return PKV_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
     const int32_t group = num_q_heads / num_kv_heads;
     if (!pkv::decode_supported(dtype, head_dim, group)) return PKV_ERR_UNSUPPORTED;
-    if (block_size % pkv::kSubTile != 0 || block_size > 256) return PKV_ERR_UNSUPPORTED;
+    if (block_size % 16 != 0 || block_size > 256) return PKV_ERR_UNSUPPORTED;
+    // sub-tile indices of the whole batch are kept in 32 bits
+    if ((int64_t)num_seqs * num_kv_heads * (((int64_t)max_context_len + 15) / 16) >= ((int64_t)1 << 31))
+        return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_ERR_ALIGN;
-    const pkv::DecodePlan plan = pkv::plan_decode(num_seqs, num_q_heads, head_dim, max_context_len);
-    if (plan.workspace_bytes > 0) {
-        if (!workspace || workspace_bytes < plan.workspace_bytes) return PKV_ERR_WORKSPACE;
-        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
-    }
+    const pkv::DecodeWorkspace ws = pkv::decode_workspace(num_seqs, num_kv_heads, group, head_dim);
+    if (!workspace || workspace_bytes < ws.bytes) return PKV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
+
+    // grid: as many waves as the GPU holds at once
+    int device = 0, cus = 0;
+    if (hipGetDevice(&device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return PKV_ERR_HIP;
+    const int per_cu = pkv::decode_waves_per_cu(dtype, head_dim, group);
+    if (per_cu <= 0 || cus <= 0) return PKV_ERR_HIP;
+    int64_t waves = (int64_t)cus * per_cu;
+    waves = waves < pkv::kMaxWaves ? waves : pkv::kMaxWaves;
+    waves -= waves % pkv::kWavesPerGroup;
+
+    char *w = static_cast<char *>(workspace);
     pkv::DecodeArgs a{};
     a.out = out;
     a.q = q;
@@ -119,22 +135,18 @@ int paged_attn_decode(void *out, const void *q, const void *k_cache, const void 
     a.v_cache = v_cache;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
-    a.ws_acc = plan.workspace_bytes
-                   ? reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_acc_offset)
-                   : nullptr;
-    a.ws_ml = plan.workspace_bytes
-                  ? reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_ml_offset)
-                  : nullptr;
+    a.ws_cnt = reinterpret_cast<int32_t *>(w + ws.cnt_offset);
+    a.ws_acc = reinterpret_cast<float *>(w + ws.acc_offset);
+    a.ws_ml = reinterpret_cast<float *>(w + ws.ml_offset);
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.block_size = block_size;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_context_len = max_context_len;
-    a.part_tokens = plan.part_tokens;
-    a.max_parts = plan.max_parts;
+    a.num_waves = (int32_t)waves;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-    return pkv::launch_attn_decode(dtype, head_dim, group, a, plan, stream) == hipSuccess
+    return pkv::launch_attn_decode(dtype, head_dim, group, a, stream) == hipSuccess
                ? PKV_OK
                : PKV_ERR_HIP;
 }

@@ -26,15 +26,12 @@ struct KvWriteArgs {
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode
-// Work split chosen on the host from sizes only (no device reads).
-struct DecodePlan {
-    int32_t part_tokens;  // tokens per partition (multiple of 16)
-    int32_t max_parts;    // partitions of the longest possible sequence
-    int32_t waves;        // waves per workgroup
-    size_t workspace_bytes;
-    size_t ws_acc_offset;  // bytes from the workspace start
-    size_t ws_ml_offset;
-};
+constexpr int kWavesPerGroup = 4;   // independent waves per workgroup
+constexpr int kMaxWaves = 8192;     // 256 CUs x 32 resident waves; sizes the workspace
+// Arrival counters sit in a region of fixed size at the start of every
+// workspace, so that partial results written by a call of one shape never
+// land where a later call of another shape expects zeroed counters.
+constexpr int64_t kMaxUnits = (int64_t)1 << 20;   // num_seqs * num_kv_heads
 
 struct DecodeArgs {
     void *out;
@@ -43,31 +40,47 @@ struct DecodeArgs {
     const void *v_cache;
     const int32_t *block_tables;
     const int32_t *context_lens;
-    float *ws_acc;  // [num_seqs][num_q_heads][max_parts][head_dim]   un-normalised
-    float *ws_ml;   // [num_seqs][num_q_heads][max_parts][2]          (max, exp-sum)
+    int32_t *ws_cnt;  // [kMaxUnits] arrival counters (first num_seqs*num_kv_heads used), zero between calls
+    float *ws_acc;    // [kMaxWaves + units][group][head_dim] un-normalised partial outputs
+    float *ws_ml;     // [kMaxWaves + units][group][2]        (max, exp-sum) per partial
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t block_size;
     int32_t max_blocks_per_seq;
     int32_t max_context_len;
-    int32_t part_tokens;
-    int32_t max_parts;
-    float scale_log2;  // scale * log2(e): scores are kept in base-2 exponent units
+    int32_t num_waves;  // waves in the grid (multiple of kWavesPerGroup, <= kMaxWaves)
+    float scale_log2;   // scale * log2(e): scores are kept in base-2 exponent units
 };
 
-constexpr int kSubTile = 16;      // tokens scored together by one wave
-constexpr int kMaxParts = 4096;   // reduce kernel keeps one weight per partition in LDS
+// Workspace layout for these sizes; offsets and total in bytes.
+struct DecodeWorkspace {
+    size_t cnt_offset;
+    size_t acc_offset;
+    size_t ml_offset;
+    size_t bytes;
+};
 
-DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                       int32_t max_context_len);
+inline DecodeWorkspace decode_workspace(int32_t num_seqs, int32_t num_kv_heads, int32_t group,
+                                        int32_t head_dim) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t units = (size_t)num_seqs * (size_t)num_kv_heads;
+    const size_t slots = (size_t)kMaxWaves + units;
+    DecodeWorkspace w{};
+    w.cnt_offset = 0;
+    w.acc_offset = (size_t)kMaxUnits * sizeof(int32_t);
+    w.ml_offset = w.acc_offset + up(slots * (size_t)group * (size_t)head_dim * sizeof(float));
+    w.bytes = w.ml_offset + up(slots * (size_t)group * 2 * sizeof(float));
+    return w;
+}
 
 bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group);
 
-// Launches the partition kernel and, when any sequence can span several
-// partitions, the merge kernel.  dtype: 0 f32, 1 f16, 2 bf16.
+// Resident waves per CU of the decode kernel for this configuration (0 on error).
+int decode_waves_per_cu(int32_t dtype, int32_t head_dim, int32_t group);
+
+// dtype: 0 f32, 1 f16, 2 bf16.
 hipError_t launch_attn_decode(int32_t dtype, int32_t head_dim, int32_t group,
-                              const DecodeArgs &a, const DecodePlan &plan,
-                              hipStream_t stream);
+                              const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace pkv

@@ -57,11 +57,18 @@ def test_status_strings(lib):
 
 def test_workspace_size_rules(lib):
     f = pkv.paged_attn_decode_workspace_size
-    assert f(64, 32, 8, 128, 16, 256) == 0            # one partition: no workspace
-    small = f(64, 32, 8, 128, 16, 2048)
-    assert small >= 64 * 32 * 8 * (128 + 2) * 4
+    # counters for every (sequence, KV head) pair, plus one partial-result slot
+    # per wave (at most 8192) and per pair, each group * (head_dim + 2) floats
+    w = f(64, 32, 8, 128, 16, 2048)
+    assert w >= (4 << 20) + (8192 + 64 * 8) * 4 * (128 + 2) * 4   # 4 MiB of counters first
+    assert w % 256 == 0
+    assert f(64, 32, 8, 128, 16, 256) == w            # independent of the context length
     assert f(4, 32, 8, 128, 16, 1 << 20) > 0
+    assert f(8, 8, 8, 64, 16, 100) < f(8, 64, 8, 64, 16, 100)   # grows with the group
     assert f(-1, 32, 8, 128, 16, 100) == 0
+    assert f(0, 32, 8, 128, 16, 100) == 0
+    assert f(4, 30, 8, 128, 16, 100) == 0             # heads not a multiple
+    assert f(65535, 32, 32, 64, 16, 100) == 0         # over 2^20 (sequence, KV head) pairs
 
 
 def _decode(lib, **kw):
@@ -90,7 +97,13 @@ def test_decode_rejects_bad_arguments_on_host(lib):
     assert _decode(lib, scale=float("nan")) == PKV_ERR_SHAPE
     assert _decode(lib, q=(1 << 12) + 2) == PKV_ERR_ALIGN
     assert _decode(lib, maxL=2048, mb=128) == PKV_ERR_WORKSPACE  # needs a workspace
+    assert _decode(lib) == PKV_ERR_WORKSPACE                     # even for short contexts
     assert _decode(lib, maxL=2048, mb=128, ws=1 << 12, wsb=16) == PKV_ERR_WORKSPACE
+    big = pkv.paged_attn_decode_workspace_size(4, 32, 8, 128, 16, 256)
+    assert _decode(lib, ws=(1 << 12) + 16, wsb=big) == PKV_ERR_ALIGN   # 256-byte alignment
+    # sub-tile counts of the batch must fit 31 bits
+    assert _decode(lib, S=65535, Hq=8, Hkv=8, mb=1 << 16, maxL=(1 << 20)) == PKV_ERR_UNSUPPORTED
+    assert _decode(lib, S=65535, Hq=32, Hkv=32) == PKV_ERR_UNSUPPORTED   # > 2^20 pairs
     assert _decode(lib, S=0) == PKV_OK                           # nothing to do
 
 

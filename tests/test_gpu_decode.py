@@ -259,3 +259,61 @@ def test_error_is_raised_not_silent():
     with pytest.raises(pkv.PKVError):
         pkv.paged_attn_decode(out, inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
                               inp.context_lens, 16, inp.scale, max_context_len=1000)
+
+
+# ---------------------------------------------------------------------------
+# the work split: equal sub-tile ranges per wave, partial results merged by the
+# last wave to arrive, arrival counters returned to zero
+# ---------------------------------------------------------------------------
+
+def test_workspace_reused_across_batches_and_left_zeroed():
+    """One workspace serves consecutive calls of different shapes; after each
+    call the arrival counters (first num_seqs*num_kv_heads int32) are zero."""
+    say("case: workspace reuse across batches")
+    first = W.build_decode_inputs([3000, 17, 900, 1, 4096, 0, 2500], 32, 8, 128, 16, "bf16", 900,
+                                  seed=21, device=DEV)
+    second = W.build_decode_inputs(list(range(1, 400, 7)), 16, 4, 128, 32, "bf16", 1200, seed=22,
+                                   device=DEV)
+    sizes = [pkv.paged_attn_decode_workspace_size(i.num_seqs, i.num_q_heads, i.num_kv_heads,
+                                                  i.head_dim, i.block_size, i.max_context_len)
+             for i in (first, second)]
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device=DEV)
+    for rep in range(2):
+        for inp in (first, second):
+            out = torch.empty_like(inp.q)
+            pkv.paged_attn_decode(out, inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                                  inp.context_lens, inp.block_size, inp.scale,
+                                  max_context_len=inp.max_context_len, workspace=ws)
+            torch.cuda.synchronize()
+            # the counter region (first 4 MiB) is zero again after every call
+            assert torch.count_nonzero(ws[: 4 << 20]).item() == 0, "arrival counters left non-zero"
+            want = oracle_step(host_inputs(inp), inp, write=False)
+            assert_close(out, want, "bf16", what=f"reuse rep {rep} S={inp.num_seqs}")
+
+
+def test_many_sequences_and_empty_ones():
+    """Over 64 sequences (the length prefix scan runs over several chunks),
+    with empty contexts interleaved."""
+    say("case: 300 sequences, some empty")
+    rng = np.random.default_rng(23)
+    lens = rng.integers(0, 120, size=300)
+    lens[::17] = 0
+    nb = int(sum(-(-int(L) // 16) for L in lens)) + 2
+    inp = W.build_decode_inputs(lens, 8, 2, 128, 16, "f16", nb, seed=23, device=DEV)
+    h = host_inputs(inp)
+    out = gpu_step(inp)
+    want = oracle_step(h, inp)
+    assert_close(out, want, "f16", what="300 seqs")
+    assert torch.all(out[torch.from_numpy(lens == 0).to(DEV)] == 0)
+
+
+def test_fewer_sub_tiles_than_waves():
+    """A single short sequence: every wave holds at most one sub-tile and the
+    unit's partial results are merged from many waves."""
+    say("case: one short sequence")
+    for L in (1, 16, 33, 250):
+        inp = W.build_decode_inputs([L], 32, 8, 128, 16, "bf16", 20, seed=24 + L, device=DEV)
+        h = host_inputs(inp)
+        out = gpu_step(inp)
+        want = oracle_step(h, inp)
+        assert_close(out, want, "bf16", what=f"L={L}")
