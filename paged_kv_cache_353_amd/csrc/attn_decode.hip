@@ -85,6 +85,7 @@ __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kDirectMerge = 8;  // units split in at most this many pieces merge in one level
 
 // ------------------------------------------------------------------ lane exchange
 // Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
@@ -411,6 +412,125 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
 
     // Leaves the unit at `u` after sub-tile `g_last`: finish it here, or hand
     // a partial result on and merge if this wave is the last to arrive.
+    // ---- partial results: records of (max, exp-sum, acc) per query head.
+    // A record holds acc[G][D] (fp32, relative to its max) and (max, exp-sum)[G].
+    constexpr int kRecAcc = G * D * 4;   // bytes of a record's acc
+    constexpr int NF = G * D / 4;        // float4 chunks of a record's acc
+    constexpr int CPL = (NF + kWave - 1) / kWave;  // chunks per lane in the flat layout
+    auto arrive = [&](int32_t *ctr) {
+        wait_vmem_done();  // this wave's record stores are complete before it counts itself
+        int old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return __builtin_amdgcn_readlane(old, 0);
+    };
+    auto reset = [&](int32_t *ctr) {
+        if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // Merges records [first, first + cnt) of a record array into the flat
+    // layout (lane holds float4 chunks lane, lane + 64, ...): returns the
+    // per-head max and exp-sum (wave-uniform) and the rescaled acc chunks.
+    // The order of every sum is fixed by the record indices.
+    auto merge_flat = [&](const float *racc, const float *rml, int64_t first, int cnt,
+                          float (&Mh)[G], float (&Lh)[G], f32x4 (&fa)[CPL]) {
+        const int hl = lane % G;  // head of this lane's (record, head) pairs in the first pass
+        float mx = kNegInf;
+        for (int pidx = lane; pidx < cnt * G; pidx += kWave) {
+            const int64_t rr = first + pidx / G;
+            mx = fmaxf(mx, __hip_atomic_load(rml + rr * G * 2 + 2 * hl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+        for (int d = G; d < kWave; d <<= 1)
+            mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ d) << 2, __builtin_bit_cast(int, mx))));
+        const float mu = mx == kNegInf ? 0.f : mx;
+        float ls = 0.f;
+        for (int pidx = lane; pidx < cnt * G; pidx += kWave) {
+            const int64_t rr = first + pidx / G;
+            const float Mr = __hip_atomic_load(rml + rr * G * 2 + 2 * hl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float Lr = __hip_atomic_load(rml + rr * G * 2 + 2 * hl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ls += fast_exp2(Mr - mu) * Lr;
+        }
+        for (int d = G; d < kWave; d <<= 1)
+            ls += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ d) << 2, __builtin_bit_cast(int, ls)));
+        static_for<0, G>([&]<int h>() {
+            Mh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mu), h));
+            Lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), h));
+        });
+        // second pass over the acc chunks, four records per batch so that
+        // their loads are in flight together
+        float Mq[CPL];   // max of the head each of this lane's chunks belongs to
+        static_for<0, CPL>([&]<int j>() {
+            const int hq = ((j * kWave + lane) * 4) / D;
+            float v = 0.f;
+            static_for<0, G>([&]<int h>() { v = hq == h ? Mh[h] : v; });
+            Mq[j] = v;
+            fa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        });
+        for (int r0 = 0; r0 < cnt; r0 += 4) {
+            f32x4 xb[4][CPL];
+            float mb[4][CPL];
+            static_for<0, 4>([&]<int b>() {
+                const int64_t rr = first + (r0 + b < cnt ? r0 + b : cnt - 1);
+                static_for<0, CPL>([&]<int j>() {
+                    const int q = j * kWave + lane;
+                    const int qc = q < NF ? q : NF - 1;
+                    xb[b][j] = load_coherent(racc + rr * G * D, kRecAcc, qc * 16);
+                    mb[b][j] = __hip_atomic_load(rml + rr * G * 2 + 2 * ((qc * 4) / D), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                });
+            });
+            static_for<0, 4>([&]<int b>() {
+                if (r0 + b < cnt) {
+                    static_for<0, CPL>([&]<int j>() {
+                        const float w = fast_exp2(mb[b][j] - Mq[j]);
+                        static_for<0, 4>([&]<int e>() { fa[j][e] = __builtin_fmaf(w, xb[b][j][e], fa[j][e]); });
+                    });
+                }
+            });
+        }
+    };
+    // Writes a merged result in the flat layout as a record (next tree level).
+    auto store_flat_record = [&](float *racc, float *rml, int64_t slot, const float (&Mh)[G],
+                                 const float (&Lh)[G], const f32x4 (&fa)[CPL]) {
+        static_for<0, CPL>([&]<int j>() {
+            const int q = j * kWave + lane;
+            if (q < NF) store_coherent(racc + slot * G * D, kRecAcc, q * 16, fa[j]);
+        });
+        static_for<0, G>([&]<int h>() {
+            if (lane == 0) {
+                __hip_atomic_store(rml + slot * G * 2 + 2 * h, Mh[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(rml + slot * G * 2 + 2 * h + 1, Lh[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        });
+    };
+    // Writes a merged result in the flat layout as the unit's output.
+    auto write_out_flat = [&](const Cursor &u, const float (&Lh)[G], const f32x4 (&fa)[CPL]) {
+        char *ob = static_cast<char *>(a.out) + ((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW;
+        static_for<0, CPL>([&]<int j>() {
+            const int q = j * kWave + lane;
+            if (q < NF) {
+                const int hq = (q * 4) / D;
+                float lq = 1.f;
+                static_for<0, G>([&]<int h>() { lq = hq == h ? Lh[h] : lq; });
+                const float inv = 1.f / lq;
+                float f[4];
+                static_for<0, 4>([&]<int e>() { f[e] = fa[j][e] * inv; });
+                if constexpr (EB == 4) {
+                    *reinterpret_cast<f32x4 *>(ob + q * 16) = f32x4{f[0], f[1], f[2], f[3]};
+                } else {
+                    float f8[8] = {f[0], f[1], f[2], f[3], 0.f, 0.f, 0.f, 0.f};
+                    const u32x4 pk = pack_chunk<DT>(f8);
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    *reinterpret_cast<u32x2 *>(ob + q * 8) = u32x2{pk[0], pk[1]};
+                }
+            }
+        });
+    };
+
+    // Leaves the unit at `u` after sub-tile `g_last`: finish it here, or hand
+    // a partial result on.  Partial results of a unit shared by k waves are
+    // merged in a two-level tree: groups of about sqrt(k) consecutive segments
+    // are merged by the last of their waves to arrive, then the group results
+    // by the last group to arrive, so that no wave reads more than about
+    // sqrt(k) records (k is known statically from the split).
     auto finish_unit = [&](const Cursor &u, int g_last) {
         combine_rows(m_run, l_run, acc, true);
         const int ua = Hkv * u.pre + u.kvh * u.n;  // unit's first sub-tile
@@ -423,71 +543,52 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         const int w_last = (int)(((int64_t)ub * Weff - 1) / T);
         const int k = w_last - w_first + 1;
         const int unit = u.seq * Hkv + u.kvh;
-        // partial record of this segment: acc[G][D] then (max, exp-sum)[G]
-        constexpr int kRecAcc = G * D * 4;
-        constexpr int kRecMl = G * 2 * 4;
+        const int64_t base = (int64_t)w_first + unit;  // slots of this unit: base .. base + k - 1
+        // this segment's record
         const int64_t slot = (int64_t)wave + unit;
-        float *pacc = a.ws_acc + slot * G * D;
-        float *pml = a.ws_ml + slot * G * 2;
-        static_for<0, G>([&]<int h>() {
-            static_for<0, NCH>([&]<int ch>() {
-                if (chunk_writer) {
-                    static_for<0, VEC / 4>([&]<int v4>() {
-                        const f32x4 x = {acc[h][ch][4 * v4], acc[h][ch][4 * v4 + 1], acc[h][ch][4 * v4 + 2],
-                                         acc[h][ch][4 * v4 + 3]};
-                        store_coherent(pacc, kRecAcc, (h * D + chunk_of(ch) * VEC + 4 * v4) * 4, x);
-                    });
-                }
-            });
-        });
-        if (rg == 0 && c < G) {
-            __hip_atomic_store(pml + 2 * c, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(pml + 2 * c + 1, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        wait_vmem_done();
-        int old = 0;
-        if (lane == 0)
-            old = __hip_atomic_fetch_add(a.ws_cnt + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __builtin_amdgcn_readlane(old, 0);
-        if (old != k - 1) return;
-        // last to arrive: merge the k records (this segment's included, read
-        // back) into the now free accumulators; row group rg takes records
-        // rg, rg+4, ... so the order is fixed whichever wave came last
-        float mm = kNegInf, ll = 0.f;
-        static_for<0, G>([&]<int h>() {
-            static_for<0, NCH>([&]<int ch>() { static_for<0, VEC>([&]<int e>() { acc[h][ch][e] = 0.f; }); });
-        });
-        for (int r = rg; r < k; r += 4) {
-            const int64_t s2 = (int64_t)(w_first + r) + unit;
-            const float *racc = a.ws_acc + s2 * G * D;
-            const float *rml = a.ws_ml + s2 * G * 2;
-            float Mr = kNegInf, Lr = 0.f;
-            if (c < G) {
-                Mr = __hip_atomic_load(rml + 2 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                Lr = __hip_atomic_load(rml + 2 * c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            const float mn = fmaxf(mm, Mr);
-            const float mu = mn == kNegInf ? 0.f : mn;
-            const float al = fast_exp2(mm - mu);
-            const float be = fast_exp2(Mr - mu);
-            ll = ll * al + Lr * be;
-            mm = mn;
+        {
+            float *pacc = a.ws_acc + slot * G * D;
+            float *pml = a.ws_ml + slot * G * 2;
             static_for<0, G>([&]<int h>() {
-                const float alh = row_bcast<h>(al);
-                const float beh = row_bcast<h>(be);
                 static_for<0, NCH>([&]<int ch>() {
-                    static_for<0, VEC / 4>([&]<int v4>() {
-                        const f32x4 x = load_coherent(racc, kRecAcc, (h * D + chunk_of(ch) * VEC + 4 * v4) * 4);
-                        static_for<0, 4>([&]<int e>() {
-                            acc[h][ch][4 * v4 + e] = acc[h][ch][4 * v4 + e] * alh + x[e] * beh;
+                    if (chunk_writer) {
+                        static_for<0, VEC / 4>([&]<int v4>() {
+                            const f32x4 x = {acc[h][ch][4 * v4], acc[h][ch][4 * v4 + 1], acc[h][ch][4 * v4 + 2],
+                                             acc[h][ch][4 * v4 + 3]};
+                            store_coherent(pacc, kRecAcc, (h * D + chunk_of(ch) * VEC + 4 * v4) * 4, x);
                         });
-                    });
+                    }
                 });
             });
+            if (rg == 0 && c < G) {
+                __hip_atomic_store(pml + 2 * c, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(pml + 2 * c + 1, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
-        combine_rows(mm, ll, acc, false);
-        write_out(u, acc, ll);
-        if (lane == 0) __hip_atomic_store(a.ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float Mh[G], Lh[G];
+        f32x4 fa[CPL];
+        if (k <= kDirectMerge) {
+            if (arrive(a.ws_cnt + unit) != k - 1) return;
+            merge_flat(a.ws_acc, a.ws_ml, base, k, Mh, Lh, fa);
+            write_out_flat(u, Lh, fa);
+            reset(a.ws_cnt + unit);
+            return;
+        }
+        int f1 = (int)__builtin_sqrtf((float)k);
+        while (f1 * f1 < k) ++f1;
+        const int ng = (k + f1 - 1) / f1;
+        const int r = wave - w_first;
+        const int j = r / f1;
+        const int kj = min(f1, k - j * f1);
+        const int64_t gslot = base + j;
+        if (arrive(a.ws_gcnt + gslot) != kj - 1) return;
+        merge_flat(a.ws_acc, a.ws_ml, base + (int64_t)j * f1, kj, Mh, Lh, fa);
+        store_flat_record(a.ws_gacc, a.ws_gml, gslot, Mh, Lh, fa);
+        reset(a.ws_gcnt + gslot);
+        if (arrive(a.ws_cnt + unit) != ng - 1) return;
+        merge_flat(a.ws_gacc, a.ws_gml, base, ng, Mh, Lh, fa);
+        write_out_flat(u, Lh, fa);
+        reset(a.ws_cnt + unit);
     };
 
     // One sub-tile: scores on MFMA, four-stream online softmax, acc += p V.

@@ -136,8 +136,11 @@ int paged_attn_decode(void *out, const void *q, const void *k_cache, const void 
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.ws_cnt = reinterpret_cast<int32_t *>(w + ws.cnt_offset);
+    a.ws_gcnt = reinterpret_cast<int32_t *>(w + ws.gcnt_offset);
     a.ws_acc = reinterpret_cast<float *>(w + ws.acc_offset);
     a.ws_ml = reinterpret_cast<float *>(w + ws.ml_offset);
+    a.ws_gacc = reinterpret_cast<float *>(w + ws.gacc_offset);
+    a.ws_gml = reinterpret_cast<float *>(w + ws.gml_offset);
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;

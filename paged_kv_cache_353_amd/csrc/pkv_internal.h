@@ -40,9 +40,12 @@ struct DecodeArgs {
     const void *v_cache;
     const int32_t *block_tables;
     const int32_t *context_lens;
-    int32_t *ws_cnt;  // [kMaxUnits] arrival counters (first num_seqs*num_kv_heads used), zero between calls
-    float *ws_acc;    // [kMaxWaves + units][group][head_dim] un-normalised partial outputs
-    float *ws_ml;     // [kMaxWaves + units][group][2]        (max, exp-sum) per partial
+    int32_t *ws_cnt;   // [kMaxUnits] per-unit arrival counters, zero between calls
+    int32_t *ws_gcnt;  // [kMaxWaves + kMaxUnits] per-group arrival counters, zero between calls
+    float *ws_acc;     // [kMaxWaves + units][group][head_dim] partial outputs (one per segment)
+    float *ws_ml;      // [kMaxWaves + units][group][2]        (max, exp-sum) of each
+    float *ws_gacc;    // [kMaxWaves + units][group][head_dim] merged groups of segments
+    float *ws_gml;     // [kMaxWaves + units][group][2]
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -53,11 +56,16 @@ struct DecodeArgs {
     float scale_log2;   // scale * log2(e): scores are kept in base-2 exponent units
 };
 
-// Workspace layout for these sizes; offsets and total in bytes.
+// Workspace layout for these sizes; offsets and total in bytes.  The
+// counters come first, in a region whose size does not depend on the sizes.
+constexpr size_t kCounterBytes = ((size_t)kMaxUnits + (size_t)kMaxWaves + (size_t)kMaxUnits) * sizeof(int32_t);
 struct DecodeWorkspace {
     size_t cnt_offset;
+    size_t gcnt_offset;
     size_t acc_offset;
     size_t ml_offset;
+    size_t gacc_offset;
+    size_t gml_offset;
     size_t bytes;
 };
 
@@ -66,11 +74,16 @@ inline DecodeWorkspace decode_workspace(int32_t num_seqs, int32_t num_kv_heads, 
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t units = (size_t)num_seqs * (size_t)num_kv_heads;
     const size_t slots = (size_t)kMaxWaves + units;
+    const size_t acc_bytes = up(slots * (size_t)group * (size_t)head_dim * sizeof(float));
+    const size_t ml_bytes = up(slots * (size_t)group * 2 * sizeof(float));
     DecodeWorkspace w{};
     w.cnt_offset = 0;
-    w.acc_offset = (size_t)kMaxUnits * sizeof(int32_t);
-    w.ml_offset = w.acc_offset + up(slots * (size_t)group * (size_t)head_dim * sizeof(float));
-    w.bytes = w.ml_offset + up(slots * (size_t)group * 2 * sizeof(float));
+    w.gcnt_offset = (size_t)kMaxUnits * sizeof(int32_t);
+    w.acc_offset = up(kCounterBytes);
+    w.ml_offset = w.acc_offset + acc_bytes;
+    w.gacc_offset = w.ml_offset + ml_bytes;
+    w.gml_offset = w.gacc_offset + acc_bytes;
+    w.bytes = w.gml_offset + ml_bytes;
     return w;
 }
 
