@@ -82,10 +82,20 @@ __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(fl
 __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
+// Values the compiler cannot prove wave-uniform are pinned to scalar
+// registers; a buffer descriptor built from a per-lane value would be
+// wrapped in a waterfall loop around every load.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+    const uint64_t v = (uint64_t)x;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kDirectMerge = 8;  // units split in at most this many pieces merge in one level
+constexpr int kDepth = 2;        // sub-tiles in flight per wave
 
 // ------------------------------------------------------------------ lane exchange
 // Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
@@ -332,9 +342,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         rows = live ? rows : 0;
         const const_i32_ptr table = (const_i32_ptr)(a.block_tables + (int64_t)u.seq * a.max_blocks_per_seq);
         const int64_t phys = table[j];
-        const int64_t off = phys * block_bytes + (int64_t)u.kvh * head_bytes + (int64_t)row0 * ROW;
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kc + off), 0, rows * ROW, kBufferFlags);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vc + off), 0, rows * ROW, kBufferFlags);
+        const int64_t off = uniform(phys * block_bytes + (int64_t)u.kvh * head_bytes + (int64_t)row0 * ROW);
+        const int nbytes = uniform(rows * ROW);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kc + off), 0, nbytes, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vc + off), 0, nbytes, kBufferFlags);
         static_for<0, NL>([&]<int b>() { kr[b] = load_chunk(rk, koff + 64 * b); });
         static_for<0, NL>([&]<int m>() { vr[m] = load_chunk(rv, voff + 256 * m); });
         // keep the compute of the previous sub-tile (and its waits) after these
@@ -350,7 +361,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     int seg_first = g0;           // first sub-tile of the current segment
 
     auto start_unit = [&](const Cursor &u) {
-        const char *qb = static_cast<const char *>(a.q) + ((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW;
+        const char *qb = static_cast<const char *>(a.q) + uniform(((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW);
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, G * ROW, kBufferFlags);
         const int qoff = c * ROW + 16 * rg;  // head c (out of range, so zero, for c >= G)
         static_for<0, NL>([&]<int b>() { qr[b] = load_chunk(rq, qoff + 64 * b); });
@@ -632,42 +643,67 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     };
 
     // ---- main loop over [g0, g1): one outer iteration per segment (the part
-    // of a unit inside this range).  The inner loop keeps two sub-tiles in
-    // flight and issues loads unconditionally (empty ranges past the end), so
-    // its waits only ever cover the sub-tile being consumed; the first
-    // sub-tile of the next segment is already in flight when a segment ends.
-    u32x4 ka[NL], va[NL], kb[NL], vb[NL];
-    Cursor cp = cur;   // sub-tile g, held in ka/va
-    Cursor cl = cur;   // most recently issued sub-tile
-    issue(cl, true, ka, va);
+    // of a unit inside this range).  kDepth sub-tiles are in flight: the inner
+    // loop issues the loads of sub-tile g + kDepth - 1 before it consumes
+    // sub-tile g, unconditionally (empty ranges past the end), so its waits
+    // only ever cover the sub-tile being consumed.  The first sub-tiles of the
+    // next segment are already in flight when a segment ends.
+    u32x4 kbuf[kDepth][NL], vbuf[kDepth][NL];
+    Cursor cp = cur;   // the sub-tile being consumed (g), in buffer 0 at a segment start
+    Cursor cl = cur;   // the most recently issued sub-tile ...
+    int gl = g0;       // ... and its index
+    issue(cl, true, kbuf[0], vbuf[0]);
+    static_for<1, kDepth - 1>([&]<int m>() {
+        const bool more = gl + 1 < g1;
+        if (more) {
+            advance(cl);
+            ++gl;
+        }
+        issue(cl, more, kbuf[m], vbuf[m]);
+    });
     int g = g0;
     while (true) {
         start_unit(cp);
         seg_first = g;
-        bool next_in_b;
-        while (true) {
-            bool more = g + 1 < g1;
-            if (more) advance(cl);
-            issue(cl, more, kb, vb);
-            process(cp, ka, va);
-            if (cp.sub + 1 == cp.n || !more) { next_in_b = true; break; }
-            cp = cl;
-            ++g;
-            more = g + 1 < g1;
-            if (more) advance(cl);
-            issue(cl, more, ka, va);
-            process(cp, kb, vb);
-            if (cp.sub + 1 == cp.n || !more) { next_in_b = false; break; }
-            cp = cl;
-            ++g;
+        int brk = 0;
+        bool done = false;
+        while (!done) {
+            static_for<0, kDepth>([&]<int i>() {
+                if (done) return;
+                constexpr int nb = (i + kDepth - 1) % kDepth;
+                const bool more = gl + 1 < g1;
+                if (more) {
+                    advance(cl);
+                    ++gl;
+                }
+                issue(cl, more, kbuf[nb], vbuf[nb]);
+                process(cp, kbuf[i], vbuf[i]);
+                if (cp.sub + 1 == cp.n || g + 1 == g1) {
+                    brk = i;
+                    done = true;
+                    return;
+                }
+                advance(cp);
+                ++g;
+            });
         }
         finish_unit(cp, g);
         if (g + 1 >= g1) break;
+        advance(cp);
         ++g;
-        cp = cl;
-        if (next_in_b) {
-            static_for<0, NL>([&]<int b>() { ka[b] = kb[b]; va[b] = vb[b]; });
-        }
+        // the next sub-tile sits in buffer brk + 1: rotate it to buffer 0
+        static_for<0, kDepth - 1>([&]<int b>() {
+            if (brk == b) {
+                u32x4 tk[kDepth][NL], tv[kDepth][NL];
+                static_for<0, kDepth>([&]<int m>() {
+                    static_for<0, NL>([&]<int e>() { tk[m][e] = kbuf[m][e]; tv[m][e] = vbuf[m][e]; });
+                });
+                static_for<0, kDepth - 1>([&]<int m>() {
+                    constexpr int from = (b + 1 + m) % kDepth;
+                    static_for<0, NL>([&]<int e>() { kbuf[m][e] = tk[from][e]; vbuf[m][e] = tv[from][e]; });
+                });
+            }
+        });
     }
 }
 

@@ -121,8 +121,9 @@ int paged_attn_decode(void *out, const void *q, const void *k_cache, const void 
     if (hipGetDevice(&device) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
         return PKV_ERR_HIP;
-    const int per_cu = pkv::decode_waves_per_cu(dtype, head_dim, group);
+    int per_cu = pkv::decode_waves_per_cu(dtype, head_dim, group);
     if (per_cu <= 0 || cus <= 0) return PKV_ERR_HIP;
+    per_cu = per_cu < 4 * pkv::kWavesPerSimd ? per_cu : 4 * pkv::kWavesPerSimd;
     int64_t waves = (int64_t)cus * per_cu;
     waves = waves < pkv::kMaxWaves ? waves : pkv::kMaxWaves;
     waves -= waves % pkv::kWavesPerGroup;

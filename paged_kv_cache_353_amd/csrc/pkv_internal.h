@@ -27,6 +27,7 @@ hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode
 constexpr int kWavesPerGroup = 4;   // independent waves per workgroup
+constexpr int kWavesPerSimd = 2;    // resident waves per SIMD the grid is sized for (at most)
 constexpr int kMaxWaves = 8192;     // 256 CUs x 32 resident waves; sizes the workspace
 // Arrival counters sit in a region of fixed size at the start of every
 // workspace, so that partial results written by a call of one shape never
