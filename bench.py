@@ -31,13 +31,16 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 METRIC = "decode-attn KV-read GB/s and % of MI355X HBM peak; query tokens/s"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["paged_kv_cache_353_amd/csrc/attn_decode.hip"]
+CSRC = os.path.join(ROOT, "paged_kv_cache_353_amd", "csrc")
 
 
 def source_digest() -> str:
+    """Digest of every source the library is built from: counter readings
+    taken on another version of the kernels are not reported."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
+    paths = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)) + [os.path.join(ROOT, "include", "pkv.h")]
+    for p in paths:
+        with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -68,17 +71,25 @@ def replicas(inp, n: int):
 
 
 def traffic_for(workload: str):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
-    None when absent or taken on an older version of the kernel source."""
-    path = os.path.join(PROFILES, "traffic.json")
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary of this workload (FETCH_SIZE and WRITE_SIZE, scaled by what the
+    same counters read for a copy of known size), or None when there is none
+    or it was taken on another version of the kernel sources."""
+    path = os.path.join(PROFILES, f"attn_decode_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as f:
-        data = json.load(f)
-    rec = data.get(workload)
-    if not rec or rec.get("source_digest") != source_digest():
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source") != source_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parity_check(inp, out, pairs):
@@ -103,8 +114,9 @@ def parity_check(inp, out, pairs):
 
 
 def cpu_baseline(inp, budget_s: float):
-    """The fp64 oracle timed on this host's cores over the first n sequences
-    of the same workload (append + decode, every query head)."""
+    """The fp64 oracle, as it stands, timed on this host's cores over whole
+    passes of the same workload (append of the step's tokens, then decode of
+    every sequence and query head), repeated until about budget_s seconds."""
     import numpy as np
     import oracle
     from paged_kv_cache_353_amd.workloads import to_numpy_bits
@@ -120,27 +132,22 @@ def cpu_baseline(inp, budget_s: float):
     tables = inp.block_tables.cpu().numpy()
     lens = inp.context_lens.cpu().numpy()
     slots = inp.slot_mapping.cpu().numpy()
-    Hq = inp.num_q_heads
-    done, tokens, t_total = 0, 0, 0.0
-    t0 = time.perf_counter()
-    kc2, vc2 = oracle.paged_kv_write(kn, vn, kc, vc, slots)
-    t_write = time.perf_counter() - t0
-    t_total += t_write
-    while done < inp.num_seqs and t_total < budget_s:
+    passes, t_total = 0, 0.0
+    while passes == 0 or t_total < budget_s:
         t0 = time.perf_counter()
-        oracle.paged_attn_decode(q, kc2, vc2, tables, lens, inp.block_size, inp.scale, inp.dtype,
-                                 pairs=[(done, h) for h in range(Hq)])
+        kc2, vc2 = oracle.paged_kv_write(kn, vn, kc, vc, slots)
+        oracle.paged_attn_decode(q, kc2, vc2, tables, lens, inp.block_size, inp.scale, inp.dtype)
         t_total += time.perf_counter() - t0
-        tokens += int(lens[done])
-        done += 1
-    kv_bytes = tokens * inp.num_kv_heads * inp.head_dim * 2 * (4 if inp.dtype == "f32" else 2)
-    return {"value": done / t_total, "unit": "query tokens/s", "cores": threads,
+        passes += 1
+    seqs = passes * inp.num_seqs
+    kv_bytes = passes * int(lens.sum()) * inp.num_kv_heads * inp.head_dim * 2 * (4 if inp.dtype == "f32" else 2)
+    return {"value": round(seqs / t_total, 2), "unit": "query tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": (f"first {done} of {inp.num_seqs} sequences of the same workload "
-                       f"(append + decode, all {Hq} query heads; the append copies the whole "
-                       f"pool once), {t_total:.1f} s on {len(os.sched_getaffinity(0))} host cores"),
-            "kv_read_gbs": kv_bytes / t_total / 1e9,
-            "seconds": t_total}
+            "sample": (f"{passes} whole pass(es) of the same workload ({inp.num_seqs} sequences, "
+                       f"all {inp.num_q_heads} query heads, append then decode) in {t_total:.1f} s; "
+                       f"{len(os.sched_getaffinity(0))} host cores visible"),
+            "kv_read_gbs": round(kv_bytes / t_total / 1e9, 4),
+            "seconds": round(t_total, 3)}
 
 
 def main() -> int:
@@ -150,7 +157,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--sets", type=int, default=4, help="rotating input copies (cold-cache timing)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle timing")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args()
@@ -226,6 +233,20 @@ def main() -> int:
     decode_us = sum(e[1].elapsed_time(e[2]) for e in ev) / K * 1e3
     decode_sorted = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in ev)
 
+    # the decode launch alone: K launches back to back over the rotating pool
+    # copies (still cold), bracketed by events on the stream they run on, so
+    # the average covers the kernel and not the gap after the append
+    launch = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    launch[0].record(stream)
+    for k in range(K):
+        s = sets[k % nsets]
+        pkv.paged_attn_decode(outs[k % nsets], s.q, s.k_cache, s.v_cache, s.block_tables,
+                              s.context_lens, s.block_size, s.scale, max_context_len=maxL,
+                              workspace=workspace)
+    launch[1].record(stream)
+    torch.cuda.synchronize()
+    launch_us = launch[0].elapsed_time(launch[1]) / K * 1e3
+
     # warm (single set, back to back) decode time, for context
     warm = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     warm[0].record(stream)
@@ -238,8 +259,8 @@ def main() -> int:
     warm_us = warm[0].elapsed_time(warm[1]) / 20 * 1e3
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
-    achieved = kv_bytes / (decode_us * 1e-6) / 1e9
-    traffic = traffic_for(args.workload)
+    achieved = kv_bytes / (launch_us * 1e-6) / 1e9
+    traffic = traffic_for(base.name)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -260,12 +281,13 @@ def main() -> int:
         "query_tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_us": round(decode_us, 3),
+        "decode_launch_us": round(launch_us, 3),
         "decode_us_p10_p90": [round(decode_sorted[len(decode_sorted) // 10], 3),
                               round(decode_sorted[(9 * len(decode_sorted)) // 10], 3)],
         "kv_write_us": round(write_us, 3),
         "warm_decode_us": round(warm_us, 3),
         "wall_s": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": "paged_attn_decode (partition + merge kernels)",
+        "roofline": {"bound": "hbm", "kernel": "attn_stream_kernel (paged_attn_decode, one launch)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "parity_worst_normwise": worst,

@@ -98,12 +98,17 @@ int paged_kv_write(const void *k, const void *v, void *k_cache, void *v_cache,
  * into equal pieces, one per wave the GPU runs at once; a (sequence, KV head)
  * pair whose context is split between waves leaves one partial result per
  * piece here (running max, exp-sum and un-normalised output, fp32), merged by
- * the last wave to finish, which it finds through a per-pair arrival counter.
- * The counters occupy the first 4 MiB of every workspace (2^20 of them, so
+ * the last wave to finish, which it finds through arrival counters (one per
+ * pair, one per group of pieces).  The counters occupy the first
+ * PKV_DECODE_COUNTER_BYTES bytes of every workspace, whatever the sizes (so
  * num_seqs * num_kv_heads <= 2^20); partial results follow.  The size depends
  * on num_seqs, num_kv_heads, the group size and head_dim; block_size and
  * max_context_len are accepted for symmetry with the decode call.
  */
+/* Bytes at the start of every decode workspace that hold arrival counters:
+ * (2^20 + 8192 + 2^20) int32. */
+#define PKV_DECODE_COUNTER_BYTES ((size_t)8421376)
+
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t block_size, int32_t max_context_len);
@@ -129,12 +134,12 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *   num_seqs * num_kv_heads <= 2^20 and
  *   num_seqs * num_kv_heads * ceil(max_context_len / 16) < 2^31
  *   workspace: >= paged_attn_decode_workspace_size(...) bytes of device memory,
- *              256-byte aligned, zero-filled once before its first use (at
- *              least its first 4 MiB).  Every call returns the counters to zero
- *              (the rest needs no initialisation), so one workspace serves any
- *              number of later calls, of any shape it is large enough for, on
- *              the same stream; calls that may run at the same time need
- *              separate workspaces.
+ *              256-byte aligned, whose first PKV_DECODE_COUNTER_BYTES bytes are
+ *              zero-filled once before its first use.  Every call returns them
+ *              to zero (the rest needs no initialisation), so one workspace
+ *              serves any number of later calls, of any shape it is large
+ *              enough for, on the same stream; calls that may run at the same
+ *              time need separate workspaces.
  * Results depend only on the logical contents and the sizes (and on the GPU's
  * compute-unit count, which fixes how work is split): they are bitwise
  * reproducible and do not change when blocks are relabelled or resized.

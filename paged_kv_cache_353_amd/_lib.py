@@ -135,10 +135,10 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     upper bound that needs no device read); context lengths are clamped to it.
     ``workspace`` (uint8, on the device, at least
     ``paged_attn_decode_workspace_size(...)`` bytes) holds partial results and
-    per-(sequence, KV head) arrival counters.  A caller-provided workspace must
-    be zero-filled once before its first use; every call returns the counters
-    to zero, so it can be reused by later calls on the same stream (not by
-    calls that run concurrently).  When not given, a zeroed one is allocated through
+    arrival counters in its first 8,421,376 bytes.  A caller-provided workspace
+    must have that region zero-filled once before its first use; every call
+    returns the counters to zero, so it can be reused by later calls on the
+    same stream (not by calls that run concurrently).  When not given, a zeroed one is allocated through
     torch.  Returns ``out``.
     """
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:

@@ -7,9 +7,11 @@
 
 #include "pkv_internal.h"
 
+static_assert(pkv::kCounterBytes == PKV_DECODE_COUNTER_BYTES, "header and library agree on the counter region");
+
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: one-launch decode, counter region in the workspace
 
 int elem_bytes(int32_t dtype) {
     switch (dtype) {

@@ -60,6 +60,7 @@ struct DecodeArgs {
 // Workspace layout for these sizes; offsets and total in bytes.  The
 // counters come first, in a region whose size does not depend on the sizes.
 constexpr size_t kCounterBytes = ((size_t)kMaxUnits + (size_t)kMaxWaves + (size_t)kMaxUnits) * sizeof(int32_t);
+static_assert(kCounterBytes % 256 == 0, "partial results start 256-byte aligned");
 struct DecodeWorkspace {
     size_t cnt_offset;
     size_t gcnt_offset;

@@ -32,6 +32,15 @@ def declared_functions():
     return sorted(set(n for n in names if n not in ("if", "defined")))
 
 
+COUNTER_BYTES = 8421376
+
+
+def test_header_counter_region_constant():
+    src = open(HEADER).read()
+    m = re.search(r"#define PKV_DECODE_COUNTER_BYTES \(\(size_t\)(\d+)\)", src)
+    assert m and int(m.group(1)) == COUNTER_BYTES == (2 ** 20 + 8192 + 2 ** 20) * 4
+
+
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("paged_kv_write", "paged_attn_decode", "paged_attn_decode_workspace_size",
@@ -60,7 +69,8 @@ def test_workspace_size_rules(lib):
     # counters for every (sequence, KV head) pair, plus one partial-result slot
     # per wave (at most 8192) and per pair, each group * (head_dim + 2) floats
     w = f(64, 32, 8, 128, 16, 2048)
-    assert w >= (4 << 20) + (8192 + 64 * 8) * 4 * (128 + 2) * 4   # 4 MiB of counters first
+    # counters first, then two sets of partial-result slots
+    assert w >= COUNTER_BYTES + 2 * (8192 + 64 * 8) * 4 * (128 + 2) * 4
     assert w % 256 == 0
     assert f(64, 32, 8, 128, 16, 256) == w            # independent of the context length
     assert f(4, 32, 8, 128, 16, 1 << 20) > 0
