@@ -1,8 +1,10 @@
 """Benchmark of the paged decode step on one MI355X.
 
 A step is one pass of the whole hot path over one batch: append each
-sequence's new token to the paged cache (paged_kv_write), then decode
-attention of one query token per sequence over its cache (paged_attn_decode).
+sequence's new token to the paged cache and decode attention of one query
+token per sequence over its cache, in one launch (paged_decode_step).  The
+same work as two launches (paged_kv_write, then paged_attn_decode) and the
+decode alone are timed for context.
 The default workload is the Llama-8B-shaped batch: 64 sequences with context
 lengths uniform in [128, 2048], 32 query / 8 KV heads, head_dim 128, block
 size 16, bf16, blocks shuffled through an 8192-block pool.
@@ -191,6 +193,13 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def step(s, out):
+        """One pass of the hot path: append + decode in one launch."""
+        pkv.paged_decode_step(out, s.q, s.k_new, s.v_new, s.k_cache, s.v_cache, s.block_tables,
+                              s.context_lens, s.block_size, s.scale, max_context_len=maxL,
+                              workspace=workspace)
+
+    def separate(s, out):
+        """The same step as two calls: paged_kv_write, then paged_attn_decode."""
         pkv.paged_kv_write(s.k_new, s.v_new, s.k_cache, s.v_cache, s.slot_mapping)
         pkv.paged_attn_decode(out, s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
                               s.block_size, s.scale, max_context_len=maxL, workspace=workspace)
@@ -208,52 +217,34 @@ def main() -> int:
         step(sets[k % nsets], outs[k % nsets])
     torch.cuda.synchronize()
 
+    def timed(fn, n):
+        """Average microseconds per call of fn over n calls back to back on
+        the rotating copies, with events on the stream the kernels run on."""
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        e[0].record(stream)
+        for k in range(n):
+            fn(sets[k % nsets], outs[k % nsets])
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / n * 1e3
+
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     w0 = time.perf_counter()
-    e0.record(stream)
-    for k in range(K):
-        s = sets[k % nsets]
-        ev[k][0].record(stream)
-        pkv.paged_kv_write(s.k_new, s.v_new, s.k_cache, s.v_cache, s.slot_mapping)
-        ev[k][1].record(stream)
-        pkv.paged_attn_decode(outs[k % nsets], s.q, s.k_cache, s.v_cache, s.block_tables,
-                              s.context_lens, s.block_size, s.scale, max_context_len=maxL,
-                              workspace=workspace)
-        ev[k][2].record(stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    step_us = timed(step, K)          # the timed region: K steps
     wall = time.perf_counter() - w0
+    ms_step = step_us * 1e-3
+    launch_us = step_us               # one launch per step
+    separate_us = timed(separate, K)  # context: the same work as two launches
+    decode_only_us = timed(lambda s, o: pkv.paged_attn_decode(
+        o, s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens, s.block_size, s.scale,
+        max_context_len=maxL, workspace=workspace), K)
 
-    ms_step = e0.elapsed_time(e1) / K
-    write_us = sum(e[0].elapsed_time(e[1]) for e in ev) / K * 1e3
-    decode_us = sum(e[1].elapsed_time(e[2]) for e in ev) / K * 1e3
-    decode_sorted = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in ev)
-
-    # the decode launch alone: K launches back to back over the rotating pool
-    # copies (still cold), bracketed by events on the stream they run on, so
-    # the average covers the kernel and not the gap after the append
-    launch = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    launch[0].record(stream)
-    for k in range(K):
-        s = sets[k % nsets]
-        pkv.paged_attn_decode(outs[k % nsets], s.q, s.k_cache, s.v_cache, s.block_tables,
-                              s.context_lens, s.block_size, s.scale, max_context_len=maxL,
-                              workspace=workspace)
-    launch[1].record(stream)
-    torch.cuda.synchronize()
-    launch_us = launch[0].elapsed_time(launch[1]) / K * 1e3
-
-    # warm (single set, back to back) decode time, for context
+    # warm (single set, back to back) step time, for context
     warm = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     warm[0].record(stream)
     for _ in range(20):
-        pkv.paged_attn_decode(outs[0], base.q, base.k_cache, base.v_cache, base.block_tables,
-                              base.context_lens, base.block_size, base.scale,
-                              max_context_len=maxL, workspace=workspace)
+        step(base, outs[0])
     warm[1].record(stream)
     torch.cuda.synchronize()
     warm_us = warm[0].elapsed_time(warm[1]) / 20 * 1e3
@@ -280,14 +271,12 @@ def main() -> int:
                    "kv_read_bytes_per_step": kv_bytes, "input_sets": nsets},
         "query_tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "decode_us": round(decode_us, 3),
-        "decode_launch_us": round(launch_us, 3),
-        "decode_us_p10_p90": [round(decode_sorted[len(decode_sorted) // 10], 3),
-                              round(decode_sorted[(9 * len(decode_sorted)) // 10], 3)],
-        "kv_write_us": round(write_us, 3),
-        "warm_decode_us": round(warm_us, 3),
+        "step_launch_us": round(launch_us, 3),
+        "separate_write_then_decode_us": round(separate_us, 3),
+        "decode_only_us": round(decode_only_us, 3),
+        "warm_step_us": round(warm_us, 3),
         "wall_s": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": "attn_stream_kernel (paged_attn_decode, one launch)",
+        "roofline": {"bound": "hbm", "kernel": "attn_stream_kernel (paged_decode_step: append + decode, one launch)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "parity_worst_normwise": worst,

@@ -152,6 +152,33 @@ int paged_attn_decode(void *out, const void *q, const void *k_cache, const void 
                       int32_t dtype, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/*
+ * paged_decode_step -- one decode step in one launch: append each sequence's
+ * new token to the cache and attend over the context including it.
+ *
+ * For every sequence i with L = context_lens[i] >= 1, the new token sits at
+ * position L - 1: its K/V (k_new[i], v_new[i]) are written to that position's
+ * slot, block_tables[i][(L-1) / block_size] * block_size + (L-1) % block_size
+ * (a token goes into the next slot of the last block, "PagedAttention核心思想"
+ * section 2.4.2), and
+ *   out[i,h,:] = sum_t softmax(s)_t * V_t,  t in [0, L),
+ * exactly as paged_kv_write followed by paged_attn_decode would give, with the
+ * new token's K/V taken from k_new/v_new (so nothing reads the slot while it
+ * is being written).  L == 0 gives out[i] = 0 and writes nothing.
+ *
+ *   k_new, v_new   [num_seqs, num_kv_heads, head_dim], contiguous, 16-byte
+ *                  aligned, same dtype as the caches
+ *   other arguments, preconditions and the workspace as for paged_attn_decode;
+ *   in addition, block_tables[i] holds the block of position L - 1.
+ */
+int paged_decode_step(void *out, const void *q, const void *k_new, const void *v_new,
+                      void *k_cache, void *v_cache, const int32_t *block_tables,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                      float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,6 +66,10 @@ def load_library() -> ctypes.CDLL:
                                           c_i32, c_i32, c_i32, c_i64, c_i32, c_f, c_i32,
                                           c_p, c_sz, c_p]
         lib.paged_attn_decode.restype = c_int
+        lib.paged_decode_step.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32,
+                                          c_i32, c_i32, c_i32, c_i32, c_i64, c_i32, c_f, c_i32,
+                                          c_p, c_sz, c_p]
+        lib.paged_decode_step.restype = c_int
         _lib = lib
         return lib
 
@@ -121,6 +125,59 @@ def paged_attn_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_hea
                                                     head_dim, block_size, max_context_len))
 
 
+def _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, block_size):
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != q.shape[0] or context_lens.shape != (q.shape[0],):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
+    for t in (out, q, k_cache, v_cache, block_tables, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if int(block_size) != k_cache.shape[2]:
+        raise ValueError("block_size must equal k_cache.shape[2]")
+
+
+def paged_decode_step(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, block_size: int, scale: float,
+                      max_context_len: Optional[int] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step in one launch: write each sequence's new token
+    (``k_new``/``v_new``, [num_seqs, num_kv_heads, head_dim]) to position
+    ``context_lens[i] - 1`` of its cache and attend over ``[0, context_lens[i])``.
+    Other arguments as for ``paged_attn_decode``.  Returns ``out``."""
+    _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, block_size)
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    if k_new.shape != (S, hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise TypeError("k_new/v_new must have the caches' dtype")
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("k_new and v_new must be contiguous")
+    mb = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mb * bs
+    lib = load_library()
+    need = int(lib.paged_attn_decode_workspace_size(S, hq, hkv, d, bs, int(max_context_len)))
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.paged_decode_step(
+            out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, hq, hkv, d,
+            bs, mb, nb, int(max_context_len), float(scale), _dtype_code(q),
+            workspace.data_ptr() if workspace.numel() else None, workspace.numel(),
+            _stream_handle(q.device)))
+    return out
+
+
 def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                       v_cache: torch.Tensor, block_tables: torch.Tensor,
                       context_lens: torch.Tensor, block_size: int, scale: float,
@@ -141,21 +198,7 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     same stream (not by calls that run concurrently).  When not given, a zeroed one is allocated through
     torch.  Returns ``out``.
     """
-    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
-    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
-        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_dim]")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise TypeError("q and the caches must share one dtype")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise TypeError("block_tables and context_lens must be int32")
-    if block_tables.dim() != 2 or block_tables.shape[0] != q.shape[0] or context_lens.shape != (q.shape[0],):
-        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
-    for t in (out, q, k_cache, v_cache, block_tables, context_lens):
-        if not t.is_contiguous():
-            raise ValueError("all tensors must be contiguous")
-    if int(block_size) != k_cache.shape[2]:
-        raise ValueError("block_size must equal k_cache.shape[2]")
+    _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, block_size)
     S, hq, d = q.shape
     nb, hkv, bs, _ = k_cache.shape
     mb = block_tables.shape[1]

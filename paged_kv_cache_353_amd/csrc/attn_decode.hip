@@ -96,6 +96,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kDirectMerge = 8;  // units split in at most this many pieces merge in one level
 constexpr int kDepth = 2;        // sub-tiles in flight per wave
+constexpr int kWeightOld = 1;    // relative share of the first half of the grid ...
+constexpr int kWeightYoung = 1;  // ... and of the second half
 
 // ------------------------------------------------------------------ lane exchange
 // Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
@@ -228,7 +230,7 @@ struct Cursor {
     int kvh;   // KV head
     int sub;   // sub-tile inside the unit
     int n;     // sub-tiles of the unit
-    int L;     // context length of the sequence
+    int L;     // tokens of the sequence read from the cache
     int pre;   // sub-tiles of one KV head summed over the sequences before `seq`
 };
 
@@ -256,14 +258,45 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     const int W = a.num_waves;
     const const_i32_ptr lens = (const_i32_ptr)a.context_lens;
     auto clampL = [&](int L) { L = L < Lmax ? L : Lmax; return L > 0 ? L : 0; };
+    // A fused step appends each sequence's new token at position L - 1 and
+    // takes it from k_new / v_new rather than from the cache: the cache tiles
+    // cover [0, L - 1) and the new token is folded in once per unit.
+    const bool fused = a.k_new != nullptr;
+    const int fused_one = fused ? 1 : 0;
+    auto tilesL = [&](int L) {  // tokens read from the cache: L - 1 in a fused step (L >= 1)
+        L = clampL(L);
+        return L - min(L, fused_one);
+    };
+    auto slot_offset = [&](int seq, int kvh, int pos) -> int64_t {  // bytes into a cache
+        const const_i32_ptr table = (const_i32_ptr)(a.block_tables + (int64_t)seq * a.max_blocks_per_seq);
+        const int j = pos / BS;
+        return (((int64_t)table[j] * Hkv + kvh) * BS + (pos - j * BS)) * (int64_t)ROW;
+    };
 
-    // ---- empty contexts: the output is the empty sum
+    // ---- contexts with no cached token: the output is the empty sum, or in a
+    // fused step with one token, that token's value (its weight is 1); the
+    // new token is also written to its slot
     for (int i = wave; i < S; i += W) {
-        if (clampL(lens[i]) == 0) {
+        const int L = clampL(lens[i]);
+        if (L == 0) {
             u32x4 z = {0u, 0u, 0u, 0u};
             char *o = static_cast<char *>(a.out) + (int64_t)i * Hq * ROW;
             for (int off = lane * 16; off < Hq * ROW; off += kWave * 16)
                 *reinterpret_cast<u32x4 *>(o + off) = z;
+        } else if (fused && L == 1) {
+            for (int idx = lane; idx < Hkv * R; idx += kWave) {
+                const int g = idx / R, ch = idx - g * R;
+                const int64_t src = ((int64_t)i * Hkv + g) * ROW + ch * 16;
+                const u32x4 kx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.k_new) + src);
+                const u32x4 vx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.v_new) + src);
+                const int64_t dst = slot_offset(i, g, 0) + ch * 16;
+                *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_cache_w) + dst) = kx;
+                *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_cache_w) + dst) = vx;
+                static_for<0, G>([&]<int h>() {
+                    *reinterpret_cast<u32x4 *>(static_cast<char *>(a.out) +
+                                               ((int64_t)i * Hq + (int64_t)g * G + h) * ROW + ch * 16) = vx;
+                });
+            }
         }
     }
 
@@ -271,7 +304,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     int N = 0;
     for (int base = 0; base < S; base += kWave) {
         const int i = base + lane;
-        const int L = i < S ? clampL(a.context_lens[i]) : 0;
+        const int L = i < S ? tilesL(a.context_lens[i]) : 0;
         N += (L + 15) >> 4;
     }
     N = uniform(wave_sum_i(N, lane));
@@ -280,8 +313,32 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     const int T = N * Hkv;
     const int Weff = T < W ? T : W;    // every wave below Weff gets >= 1 sub-tile
     if (wave >= Weff) return;
-    const int g0 = (int)((int64_t)wave * T / Weff);
-    const int g1 = (int)((int64_t)(wave + 1) * T / Weff);
+    // Range boundaries: wave w starts at T * cum(w) / cum(Weff), where the
+    // first half of the grid (dispatched first, so older on every SIMD and
+    // favoured by the issue arbiter) may weigh kWeightOld against kWeightYoung
+    // for the second half.  Weights apply only when every range stays
+    // non-empty (at least two sub-tiles per wave); the split depends only on
+    // T and W, so results stay deterministic.
+    const bool weighted = kWeightOld != kWeightYoung && Weff == W && T >= 2 * W;
+    const int wa = weighted ? kWeightOld : 1;
+    const int wb = weighted ? kWeightYoung : 1;
+    const int half = Weff / 2;
+    auto cum = [&](int w) -> int64_t {
+        return (int64_t)wa * min(w, half) + (int64_t)wb * max(w - half, 0);
+    };
+    const int64_t cum_all = cum(Weff);
+    auto start_of = [&](int w) -> int { return (int)((int64_t)T * cum(w) / cum_all); };
+    // the wave whose range holds sub-tile x: the largest w with start_of(w) <= x
+    auto wave_of = [&](int x) -> int {
+        const int64_t t = (int64_t)x * cum_all / T;
+        int w = t <= (int64_t)wa * half ? (int)(t / wa) : half + (int)((t - (int64_t)wa * half) / wb);
+        w = min(max(w, 0), Weff - 1);
+        while (w + 1 < Weff && start_of(w + 1) <= x) ++w;
+        while (w > 0 && start_of(w) > x) --w;
+        return w;
+    };
+    const int g0 = start_of(wave);
+    const int g1 = start_of(wave + 1);
 
     // ---- locate g0: sequence (prefix scan of sub-tile counts), KV head, sub-tile
     Cursor cur{};
@@ -289,7 +346,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         int pre = 0;
         for (int base = 0; base < S; base += kWave) {
             const int i = base + lane;
-            const int L = i < S ? clampL(a.context_lens[i]) : 0;
+            const int L = i < S ? tilesL(a.context_lens[i]) : 0;
             const int n = (L + 15) >> 4;
             const int incl = wave_incl_scan(n, lane);
             const uint64_t hit = __builtin_amdgcn_ballot_w64((pre + incl) * Hkv > g0);
@@ -315,7 +372,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         u.pre += u.n;
         do {
             ++u.seq;
-            u.L = clampL(lens[u.seq]);
+            u.L = tilesL(lens[u.seq]);
         } while (u.L == 0);
         u.n = (u.L + 15) >> 4;
     };
@@ -355,6 +412,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
 
     // ---- per-unit state
     u32x4 qr[NL];                 // B operand: head = lane % 16 (zero past G)
+    u32x4 knew[NL], vnew[NL];     // fused step: the appended token, row 0 of a one-row tile
     float m_run = kNegInf;        // lane (rg, j): running max of stream rg, head j (log2 units)
     float l_run = 0.f;            // its exp-sum
     float acc[G][NCH][VEC];       // lane (rg, c): un-normalised output of stream rg
@@ -365,6 +423,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, G * ROW, kBufferFlags);
         const int qoff = c * ROW + 16 * rg;  // head c (out of range, so zero, for c >= G)
         static_for<0, NL>([&]<int b>() { qr[b] = load_chunk(rq, qoff + 64 * b); });
+        if (fused && u.sub == 0) {
+            // the new token as a one-row tile in the K and V layouts
+            const int64_t nb = uniform(((int64_t)u.seq * Hkv + u.kvh) * ROW);
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(static_cast<const char *>(a.k_new) + nb), 0, ROW, kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(static_cast<const char *>(a.v_new) + nb), 0, ROW, kBufferFlags);
+            static_for<0, NL>([&]<int b>() { knew[b] = load_chunk(rk, koff + 64 * b); });
+            static_for<0, NL>([&]<int m>() { vnew[m] = load_chunk(rv, voff + 256 * m); });
+        }
         // wait for q here, so that the sub-tile loop is entered with nothing
         // but its own loads in flight and its waits stay exact
 #pragma unroll
@@ -550,8 +618,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             write_out(u, acc, l_run);
             return;
         }
-        const int w_first = (int)(((int64_t)(ua + 1) * Weff - 1) / T);
-        const int w_last = (int)(((int64_t)ub * Weff - 1) / T);
+        const int w_first = wave_of(ua);
+        const int w_last = wave_of(ub - 1);
         const int k = w_last - w_first + 1;
         const int unit = u.seq * Hkv + u.kvh;
         const int64_t base = (int64_t)w_first + unit;  // slots of this unit: base .. base + k - 1
@@ -603,10 +671,9 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     };
 
     // One sub-tile: scores on MFMA, four-stream online softmax, acc += p V.
-    auto process = [&](const Cursor &u, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) {
+    auto process_rows = [&](int nvalid, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
         static_for<0, NL>([&]<int b>() { s = mfma_chunk<DT>(kr[b], qr[b], s); });
-        const int nvalid = u.L - (u.sub << 4);  // >= 1
         float sv[4];
         float tmax = kNegInf;
         static_for<0, 4>([&]<int r>() {
@@ -641,6 +708,23 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             });
         });
     };
+    auto process = [&](const Cursor &u, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) {
+        process_rows(u.L - (u.sub << 4), kr, vr);  // valid rows: >= 1
+    };
+    // Fused step, unit's first sub-tile: fold the appended token (position
+    // L - 1 of the sequence) into the running state and store it in its slot.
+    auto fold_new_token = [&](const Cursor &u) {
+        process_rows(1, knew, vnew);
+        const int64_t so = uniform(slot_offset(u.seq, u.kvh, u.L));
+        char *kd = static_cast<char *>(a.k_cache_w) + so;
+        char *vd = static_cast<char *>(a.v_cache_w) + so;
+        static_for<0, NL>([&]<int b>() {
+            if (koff + 64 * b < ROW) *reinterpret_cast<u32x4 *>(kd + koff + 64 * b) = knew[b];
+        });
+        static_for<0, NL>([&]<int m>() {
+            if (voff + 256 * m < ROW) *reinterpret_cast<u32x4 *>(vd + voff + 256 * m) = vnew[m];
+        });
+    };
 
     // ---- main loop over [g0, g1): one outer iteration per segment (the part
     // of a unit inside this range).  kDepth sub-tiles are in flight: the inner
@@ -664,6 +748,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     int g = g0;
     while (true) {
         start_unit(cp);
+        if (fused && cp.sub == 0) fold_new_token(cp);
         seg_first = g;
         int brk = 0;
         bool done = false;

@@ -88,13 +88,18 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
     return pkv::decode_workspace(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim).bytes;
 }
 
-int paged_attn_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
-                      const int32_t *block_tables, const int32_t *context_lens,
-                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                      int64_t num_blocks, int32_t max_context_len, float scale,
-                      int32_t dtype, void *workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by paged_attn_decode (k_new == v_new == NULL) and paged_decode_step.
+int decode_impl(void *out, const void *q, const void *k_new, const void *v_new,
+                const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
+                hipStream_t stream) {
     if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
@@ -112,8 +117,10 @@ int paged_attn_decode(void *out, const void *q, const void *k_cache, const void 
         return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
+    if ((k_new == nullptr) != (v_new == nullptr)) return PKV_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_ERR_ALIGN;
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGN;
     const pkv::DecodeWorkspace ws = pkv::decode_workspace(num_seqs, num_kv_heads, group, head_dim);
     if (!workspace || workspace_bytes < ws.bytes) return PKV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
@@ -138,6 +145,11 @@ int paged_attn_decode(void *out, const void *q, const void *k_cache, const void 
     a.v_cache = v_cache;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    // the fused step writes the appended token into the caches it was given
+    a.k_cache_w = const_cast<void *>(k_cache);
+    a.v_cache_w = const_cast<void *>(v_cache);
     a.ws_cnt = reinterpret_cast<int32_t *>(w + ws.cnt_offset);
     a.ws_gcnt = reinterpret_cast<int32_t *>(w + ws.gcnt_offset);
     a.ws_acc = reinterpret_cast<float *>(w + ws.acc_offset);
@@ -155,6 +167,37 @@ int paged_attn_decode(void *out, const void *q, const void *k_cache, const void 
     return pkv::launch_attn_decode(dtype, head_dim, group, a, stream) == hipSuccess
                ? PKV_OK
                : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                      int64_t num_blocks, int32_t max_context_len, float scale,
+                      int32_t dtype, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, max_context_len, scale, dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+int paged_decode_step(void *out, const void *q, const void *k_new, const void *v_new,
+                      void *k_cache, void *v_cache, const int32_t *block_tables,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                      float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_NULL;
+    return decode_impl(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, max_context_len, scale, dtype, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

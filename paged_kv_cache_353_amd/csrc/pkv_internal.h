@@ -41,6 +41,12 @@ struct DecodeArgs {
     const void *v_cache;
     const int32_t *block_tables;
     const int32_t *context_lens;
+    // fused step only (null otherwise): the appended tokens [num_seqs][num_kv_heads][head_dim]
+    // and the caches again, writable, for their slots
+    const void *k_new;
+    const void *v_new;
+    void *k_cache_w;
+    void *v_cache_w;
     int32_t *ws_cnt;   // [kMaxUnits] per-unit arrival counters, zero between calls
     int32_t *ws_gcnt;  // [kMaxWaves + kMaxUnits] per-group arrival counters, zero between calls
     float *ws_acc;     // [kMaxWaves + units][group][head_dim] partial outputs (one per segment)

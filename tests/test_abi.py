@@ -44,7 +44,7 @@ def test_header_counter_region_constant():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("paged_kv_write", "paged_attn_decode", "paged_attn_decode_workspace_size",
-              "pkv_status_string", "pkv_version"):
+              "paged_decode_step", "pkv_status_string", "pkv_version"):
         assert n in names
 
 
@@ -149,3 +149,21 @@ def test_python_binding_validates_before_the_library():
         pkv.paged_attn_decode(q, q, kc, kc, bt.long(), cl, block_size=16, scale=1.0)
     with pytest.raises(ValueError):
         pkv.paged_kv_write(q, q, kc, kc, torch.zeros(2, dtype=torch.int32))
+
+
+def test_decode_step_rejects_bad_arguments_on_host(lib):
+    def step(**kw):
+        a = dict(out=1 << 12, q=1 << 12, kn=1 << 12, vn=1 << 12, k=1 << 12, v=1 << 12, bt=1 << 12,
+                 cl=1 << 12, S=4, Hq=32, Hkv=8, D=128, bs=16, mb=16, nb=64, maxL=256, scale=0.1,
+                 dtype=2, ws=None, wsb=0)
+        a.update(kw)
+        return lib.paged_decode_step(a["out"], a["q"], a["kn"], a["vn"], a["k"], a["v"], a["bt"],
+                                     a["cl"], a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"],
+                                     a["nb"], a["maxL"], a["scale"], a["dtype"], a["ws"], a["wsb"],
+                                     None)
+    assert step(kn=None) == PKV_ERR_NULL
+    assert step(vn=None) == PKV_ERR_NULL
+    assert step(kn=(1 << 12) + 8) == PKV_ERR_ALIGN
+    assert step(D=96) == PKV_ERR_UNSUPPORTED
+    assert step() == PKV_ERR_WORKSPACE
+    assert step(S=0, kn=None, vn=None) == PKV_OK
