@@ -511,42 +511,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // The order of every sum is fixed by the record indices.
     auto merge_flat = [&](const float *racc, const float *rml, int64_t first, int cnt,
                           float (&Mh)[G], float (&Lh)[G], f32x4 (&fa)[CPL]) {
-        const int hl = lane % G;  // head of this lane's (record, head) pairs in the first pass
-        float mx = kNegInf;
-        for (int pidx = lane; pidx < cnt * G; pidx += kWave) {
-            const int64_t rr = first + pidx / G;
-            mx = fmaxf(mx, __hip_atomic_load(rml + rr * G * 2 + 2 * hl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        }
-        for (int d = G; d < kWave; d <<= 1)
-            mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ d) << 2, __builtin_bit_cast(int, mx))));
-        const float mu = mx == kNegInf ? 0.f : mx;
-        float ls = 0.f;
-        for (int pidx = lane; pidx < cnt * G; pidx += kWave) {
-            const int64_t rr = first + pidx / G;
-            const float Mr = __hip_atomic_load(rml + rr * G * 2 + 2 * hl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float Lr = __hip_atomic_load(rml + rr * G * 2 + 2 * hl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ls += fast_exp2(Mr - mu) * Lr;
-        }
-        for (int d = G; d < kWave; d <<= 1)
-            ls += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ d) << 2, __builtin_bit_cast(int, ls)));
-        static_for<0, G>([&]<int h>() {
-            Mh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mu), h));
-            Lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), h));
-        });
-        // second pass over the acc chunks, four records per batch so that
-        // their loads are in flight together
-        float Mq[CPL];   // max of the head each of this lane's chunks belongs to
-        static_for<0, CPL>([&]<int j>() {
-            const int hq = ((j * kWave + lane) * 4) / D;
-            float v = 0.f;
-            static_for<0, G>([&]<int h>() { v = hq == h ? Mh[h] : v; });
-            Mq[j] = v;
-            fa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        });
-        for (int r0 = 0; r0 < cnt; r0 += 4) {
-            f32x4 xb[4][CPL];
-            float mb[4][CPL];
-            static_for<0, 4>([&]<int b>() {
+        // records whose acc chunks are in flight together (fewer when a record
+        // takes more registers per lane)
+        constexpr int kBatch = CPL <= 2 ? 8 : 2;
+        const int hl = lane % G;   // head of this lane's (record, head) pairs
+        auto load_batch = [&](int r0, f32x4 (&xb)[kBatch][CPL], float (&mb)[kBatch][CPL]) {
+            static_for<0, kBatch>([&]<int b>() {
                 const int64_t rr = first + (r0 + b < cnt ? r0 + b : cnt - 1);
                 static_for<0, CPL>([&]<int j>() {
                     const int q = j * kWave + lane;
@@ -556,7 +526,55 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
                                                  __HIP_MEMORY_SCOPE_AGENT);
                 });
             });
-            static_for<0, 4>([&]<int b>() {
+        };
+        // the first pair of this lane and the first batch of acc chunks are
+        // requested together, so the common case costs one round trip
+        float m0 = kNegInf, l0 = 0.f;
+        if (lane < cnt * G) {
+            const int64_t rr = first + lane / G;
+            m0 = __hip_atomic_load(rml + rr * G * 2 + 2 * hl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            l0 = __hip_atomic_load(rml + rr * G * 2 + 2 * hl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        f32x4 xb[kBatch][CPL];
+        float mb[kBatch][CPL];
+        load_batch(0, xb, mb);
+        // per-head max and exp-sum over the records: online over this lane's
+        // pairs, then a fixed butterfly over the lanes of the same head
+        auto fold = [](float &m, float &l, float m2, float l2) {
+            const float mn = fmaxf(m, m2);
+            const float mu = mn == kNegInf ? 0.f : mn;
+            l = l * fast_exp2(m - mu) + l2 * fast_exp2(m2 - mu);
+            m = mn;
+        };
+        float mx = m0, ls = l0;
+        for (int pidx = lane + kWave; pidx < cnt * G; pidx += kWave) {
+            const int64_t rr = first + pidx / G;
+            const float Mr = __hip_atomic_load(rml + rr * G * 2 + 2 * hl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float Lr = __hip_atomic_load(rml + rr * G * 2 + 2 * hl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            fold(mx, ls, Mr, Lr);
+        }
+        for (int d = G; d < kWave; d <<= 1) {
+            const float m2 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ d) << 2, __builtin_bit_cast(int, mx)));
+            const float l2 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ d) << 2, __builtin_bit_cast(int, ls)));
+            fold(mx, ls, m2, l2);
+        }
+        const float mu = mx == kNegInf ? 0.f : mx;
+        static_for<0, G>([&]<int h>() {
+            Mh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mu), h));
+            Lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), h));
+        });
+        float Mq[CPL];   // max of the head each of this lane's chunks belongs to
+        static_for<0, CPL>([&]<int j>() {
+            const int hq = ((j * kWave + lane) * 4) / D;
+            float v = 0.f;
+            static_for<0, G>([&]<int h>() { v = hq == h ? Mh[h] : v; });
+            Mq[j] = v;
+            fa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        });
+        // weighted sum of the acc chunks, in record order
+        for (int r0 = 0; r0 < cnt; r0 += kBatch) {
+            if (r0 > 0) load_batch(r0, xb, mb);
+            static_for<0, kBatch>([&]<int b>() {
                 if (r0 + b < cnt) {
                     static_for<0, CPL>([&]<int j>() {
                         const float w = fast_exp2(mb[b][j] - Mq[j]);
