@@ -190,6 +190,7 @@ def main() -> int:
     workspace = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(s.q) for s in sets]
     kv_bytes = base.kv_read_bytes()
+    kv_unique = base.kv_unique_bytes()   # differs from kv_bytes only where blocks are shared
     stream = torch.cuda.current_stream()
 
     def step(s, out):
@@ -268,9 +269,11 @@ def main() -> int:
         "config": {"workload": base.name, "num_seqs": S, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": base.block_size,
                    "context_tokens": int(base.lens.sum()), "max_context_len": maxL,
-                   "kv_read_bytes_per_step": kv_bytes, "input_sets": nsets},
+                   "kv_read_bytes_per_step": kv_bytes, "kv_unique_bytes_per_step": kv_unique,
+                   "input_sets": nsets},
         "query_tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "unique_kv_gbs": round(kv_unique / (ms_step * 1e-3) / 1e9, 2),
         "step_launch_us": round(launch_us, 3),
         "separate_write_then_decode_us": round(separate_us, 3),
         "decode_only_us": round(decode_only_us, 3),

@@ -78,6 +78,19 @@ class DecodeInputs:
         """K and V bytes of the attended tokens, each counted once per sequence."""
         return int(self.lens.sum()) * self.num_kv_heads * self.head_dim * 2 * DTYPE_BYTES[self.dtype]
 
+    def kv_unique_bytes(self) -> int:
+        """K and V bytes of the attended tokens counted once per physical slot:
+        blocks shared by several sequences (forked prefixes) count once."""
+        tables = self.block_tables.cpu().numpy()
+        rows = {}
+        bs = self.block_size
+        for i, L in enumerate(self.lens):
+            L = int(L)
+            for j in range(-(-L // bs)):
+                b = int(tables[i, j])
+                rows[b] = max(rows.get(b, 0), min(bs, L - j * bs))
+        return sum(rows.values()) * self.num_kv_heads * self.head_dim * 2 * DTYPE_BYTES[self.dtype]
+
 
 def _randn_into(t: torch.Tensor, gen: torch.Generator, chunk_elems: int = 1 << 28) -> None:
     """Fill ``t`` (contiguous) with N(0,1) drawn in fp32, rounded to t's dtype."""

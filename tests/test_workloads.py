@@ -84,3 +84,14 @@ def test_shared_prefix_small_variant_tables():
 def test_config_builders_present():
     assert sorted(W.CONFIG_BUILDERS) == [1, 2, 3, 4, 5]
     assert W.seed_for(2) == 353_002
+
+
+def test_kv_unique_bytes_counts_shared_blocks_once():
+    inp = W.shared_prefix("cpu", prompt_len=64, num_prompts=2, samples=3, suffix_len=16,
+                          num_blocks=64, num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16)
+    per_token = 2 * 64 * 2 * 2
+    # 2 prompts of 64 tokens stored once, 6 samples with 16 private tokens each
+    assert inp.kv_unique_bytes() == (2 * 64 + 6 * 16) * per_token
+    assert inp.kv_read_bytes() == 6 * 80 * per_token
+    tiny = W.tiny("cpu")
+    assert tiny.kv_unique_bytes() == tiny.kv_read_bytes()
