@@ -93,6 +93,27 @@ int paged_kv_write(const void *k, const void *v, void *k_cache, void *v_cache,
                    int32_t dtype, hipStream_t stream);
 
 /*
+ * paged_copy_blocks -- copy whole physical blocks (copy-on-write).
+ *
+ * For every pair n with src = block_pairs[2n] >= 0 and dst = block_pairs[2n+1]
+ * >= 0, block dst of both caches becomes a bit copy of block src: every KV
+ * head and every row.  Shared blocks are read-only; a write into a block whose
+ * reference count is above one first copies it to a fresh block
+ * ("PagedAttention核心思想" section 2.4.3; "PagedAttention技术解析" section
+ * 2.1 on reference counts).  Copying the whole block leaves the valid rows
+ * identical; rows past a sequence's end are never read.
+ *
+ *   block_pairs   int64 [num_pairs][2] on the device; a negative entry skips
+ *                 the pair
+ * Preconditions (not checked, device data): ids below num_blocks; no block is
+ * the destination of two pairs, or both a source and a destination.
+ */
+int paged_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_pairs,
+                      int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int64_t num_blocks, int32_t dtype,
+                      hipStream_t stream);
+
+/*
  * Bytes of device workspace paged_attn_decode needs for these sizes (0 for
  * invalid sizes; the decode call reports those).  The work of a batch is cut
  * into equal pieces, one per wave the GPU runs at once; a (sequence, KV head)

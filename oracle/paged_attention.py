@@ -244,5 +244,30 @@ def paged_kv_write(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray,
     return kc, vc
 
 
+# ---------------------------------------------------------------------------
+# block copy (copy-on-write)
+# ---------------------------------------------------------------------------
+
+def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, block_pairs):
+    """Whole-block bit copy for copy-on-write; returns new cache arrays.
+
+    "PagedAttention核心思想" section 2.4.3: shared blocks are read-only, and a
+    write into a block referenced more than once first copies it.  Every pair
+    (src, dst) with both ids non-negative makes block ``dst`` (all KV heads,
+    all rows) a copy of block ``src``; pairs are applied in order.
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    for src, dst in block_pairs:
+        src, dst = int(src), int(dst)
+        if src < 0 or dst < 0:
+            continue
+        if not (src < kc.shape[0] and dst < kc.shape[0]):
+            raise IndexError("block id outside the pool")
+        kc[dst] = kc[src]
+        vc[dst] = vc[src]
+    return kc, vc
+
+
 __all__ = ["DTYPES", "to_f64", "physical_slot", "gather_rows", "kv_head_of",
-           "softmax_weights", "paged_attn_decode", "paged_kv_write"]
+           "softmax_weights", "paged_attn_decode", "paged_kv_write", "copy_blocks"]

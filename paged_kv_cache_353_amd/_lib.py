@@ -70,6 +70,8 @@ def load_library() -> ctypes.CDLL:
                                           c_i32, c_i32, c_i32, c_i32, c_i64, c_i32, c_f, c_i32,
                                           c_p, c_sz, c_p]
         lib.paged_decode_step.restype = c_int
+        lib.paged_copy_blocks.argtypes = [c_p, c_p, c_p, c_i64, c_i32, c_i32, c_i32, c_i64, c_i32, c_p]
+        lib.paged_copy_blocks.restype = c_int
         _lib = lib
         return lib
 
@@ -116,6 +118,24 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
             k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             slot_mapping.data_ptr(), k.shape[0], hkv, d, bs, nb, k.stride(0), v.stride(0),
             _dtype_code(k_cache), _stream_handle(k_cache.device)))
+
+
+def paged_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_pairs: torch.Tensor) -> None:
+    """Copy whole physical blocks of both caches: ``block_pairs`` is int64
+    [num_pairs, 2] of (src, dst) on the caches' device (copy-on-write)."""
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_dim] of one dtype")
+    if block_pairs.dtype != torch.int64 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int64 [num_pairs, 2]")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous() and block_pairs.is_contiguous()):
+        raise ValueError("caches and block_pairs must be contiguous")
+    nb, hkv, bs, d = k_cache.shape
+    lib = load_library()
+    with torch.cuda.device(k_cache.device):
+        _check(lib.paged_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_pairs.data_ptr(),
+                                     block_pairs.shape[0], hkv, d, bs, nb, _dtype_code(k_cache),
+                                     _stream_handle(k_cache.device)))
 
 
 def paged_attn_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,

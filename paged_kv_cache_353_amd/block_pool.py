@@ -112,6 +112,37 @@ class BlockManager:
         self.seqs.append(Sequence_(table=list(p.table), length=p.length))
         return len(self.seqs) - 1
 
+    def fork_many(self, parent: int, n: int) -> List[int]:
+        """``n`` new sequences sharing every block of ``parent`` (parallel
+        sampling or beam width ``n``): one reference count update per block."""
+        if n < 0:
+            raise ValueError("n must be non-negative")
+        p = self.seqs[parent]
+        for b in p.table:
+            if self.pool.ref[b] <= 0:
+                raise ValueError(f"block {b} is not allocated")
+            self.pool.ref[b] += n
+        first = len(self.seqs)
+        self.seqs.extend(Sequence_(table=list(p.table), length=p.length) for _ in range(n))
+        return list(range(first, first + n))
+
+    def append_batch(self, sids: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+        """One new token for each sequence of ``sids``, in order.
+
+        Returns the slot of every token (int64, the ``slot_mapping`` of the KV
+        write) and the (src, dst) block pairs to copy first (int64 [k, 2], the
+        argument of the device block copy).  Sources and destinations are
+        disjoint: a destination is freshly allocated, and a source keeps at
+        least one other reference, so it is never written in this batch.
+        """
+        slots = np.empty(len(sids), dtype=np.int64)
+        pairs = []
+        for n, sid in enumerate(sids):
+            slots[n], cow = self.append_token(sid)
+            if cow is not None:
+                pairs.append((cow.src, cow.dst))
+        return slots, np.array(pairs, dtype=np.int64).reshape(-1, 2)
+
     def append_token(self, sid: int) -> Tuple[int, Optional[CowCopy]]:
         """Reserve the slot of the sequence's next token.
 

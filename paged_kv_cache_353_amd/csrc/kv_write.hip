@@ -1,4 +1,5 @@
-// KV append: copy each new token's K/V rows into its slot of the paged cache.
+// KV append: copy each new token's K/V rows into its slot of the paged cache;
+// and the block copy that copy-on-write needs.
 //
 // "PagedAttention核心思想" section 2.4.2: a generated token is stored in the
 // next free slot of its sequence's last block (a new block is taken only when
@@ -37,7 +38,34 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a, int chunks
     *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_cache) + dst) = vx;
 }
 
+// Block copy (copy-on-write): one workgroup per (src, dst) pair moves the
+// whole block, every KV head and row, of K and of V, 16 bytes per thread per
+// step.  A block is contiguous in both caches, so reads and writes coalesce.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
+    const int64_t pair = blockIdx.x;
+    const int64_t src = a.pairs[2 * pair];
+    const int64_t dst = a.pairs[2 * pair + 1];
+    if (src < 0 || dst < 0) return;
+    const int64_t chunks = a.block_bytes / 16;
+    const char *ks = static_cast<const char *>(a.k_cache) + src * a.block_bytes;
+    const char *vs = static_cast<const char *>(a.v_cache) + src * a.block_bytes;
+    char *kd = static_cast<char *>(a.k_cache) + dst * a.block_bytes;
+    char *vd = static_cast<char *>(a.v_cache) + dst * a.block_bytes;
+    for (int64_t i = threadIdx.x; i < chunks; i += blockDim.x) {
+        const u32x4 kx = *reinterpret_cast<const u32x4 *>(ks + i * 16);
+        const u32x4 vx = *reinterpret_cast<const u32x4 *>(vs + i * 16);
+        *reinterpret_cast<u32x4 *>(kd + i * 16) = kx;
+        *reinterpret_cast<u32x4 *>(vd + i * 16) = vx;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t stream) {
+    if (a.num_pairs == 0) return hipSuccess;
+    copy_blocks_kernel<<<dim3((unsigned)a.num_pairs), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t stream) {
     const int chunks_per_row = a.head_dim * a.elem_bytes / 16;

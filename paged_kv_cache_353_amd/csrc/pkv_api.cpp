@@ -78,6 +78,28 @@ int paged_kv_write(const void *k, const void *v, void *k_cache, void *v_cache,
     return pkv::launch_kv_write(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int paged_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_pairs,
+                      int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int64_t num_blocks, int32_t dtype,
+                      hipStream_t stream) {
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return PKV_ERR_DTYPE;
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return PKV_ERR_SHAPE;
+    if (num_pairs > 0x7FFFFFFF) return PKV_ERR_SHAPE;
+    if (num_pairs == 0) return PKV_OK;
+    if (!k_cache || !v_cache || !block_pairs) return PKV_ERR_NULL;
+    const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || block_bytes % 16 != 0) return PKV_ERR_ALIGN;
+    pkv::CopyBlocksArgs a{};
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.pairs = block_pairs;
+    a.num_pairs = num_pairs;
+    a.block_bytes = block_bytes;
+    return pkv::launch_copy_blocks(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t block_size, int32_t max_context_len) {

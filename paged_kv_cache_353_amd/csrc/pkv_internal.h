@@ -25,6 +25,17 @@ struct KvWriteArgs {
 
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t stream);
 
+// ---------------------------------------------------------------- block copy
+struct CopyBlocksArgs {
+    void *k_cache;
+    void *v_cache;
+    const int64_t *pairs;  // [num_pairs][2] (src, dst); a negative entry skips the pair
+    int64_t num_pairs;
+    int64_t block_bytes;   // num_kv_heads * block_size * head_dim * elem_bytes
+};
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t stream);
+
 // ---------------------------------------------------------------- decode
 constexpr int kWavesPerGroup = 4;   // independent waves per workgroup
 constexpr int kWavesPerSimd = 2;    // resident waves per SIMD the grid is sized for (at most)

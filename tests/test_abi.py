@@ -44,7 +44,7 @@ def test_header_counter_region_constant():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("paged_kv_write", "paged_attn_decode", "paged_attn_decode_workspace_size",
-              "paged_decode_step", "pkv_status_string", "pkv_version"):
+              "paged_decode_step", "paged_copy_blocks", "pkv_status_string", "pkv_version"):
         assert n in names
 
 
@@ -167,3 +167,19 @@ def test_decode_step_rejects_bad_arguments_on_host(lib):
     assert step(D=96) == PKV_ERR_UNSUPPORTED
     assert step() == PKV_ERR_WORKSPACE
     assert step(S=0, kn=None, vn=None) == PKV_OK
+
+
+def test_copy_blocks_rejects_bad_arguments_on_host(lib):
+    def cp(**kw):
+        a = dict(k=1 << 12, v=1 << 12, p=1 << 12, n=4, Hkv=8, D=128, bs=16, nb=64, dtype=2)
+        a.update(kw)
+        return lib.paged_copy_blocks(a["k"], a["v"], a["p"], a["n"], a["Hkv"], a["D"], a["bs"],
+                                     a["nb"], a["dtype"], None)
+    assert cp(n=0, p=None) == PKV_OK                 # nothing to copy
+    assert cp(p=None) == PKV_ERR_NULL
+    assert cp(v=None) == PKV_ERR_NULL
+    assert cp(dtype=9) == PKV_ERR_DTYPE
+    assert cp(n=-1) == PKV_ERR_SHAPE
+    assert cp(bs=0) == PKV_ERR_SHAPE
+    assert cp(k=(1 << 12) + 4) == PKV_ERR_ALIGN
+    assert cp(Hkv=1, bs=1, D=2, dtype=1) == PKV_ERR_ALIGN   # 4-byte blocks

@@ -97,3 +97,30 @@ def test_waste_arithmetic_from_pages():
     for L in (1, 15, 16, 17, 128, 2047):
         assert 0 <= paged_waste_tokens(L, 16) < 16
     assert paged_waste_tokens(128, 16) == 0
+
+
+def test_fork_many_and_batched_append():
+    pool = BlockPool(64, order=np.random.default_rng(3).permutation(64))
+    mgr = BlockManager(pool, block_size=4)
+    root = mgr.new_sequence()
+    for _ in range(10):                    # 2 full blocks + 2 tokens
+        mgr.append_token(root)
+    kids = mgr.fork_many(root, 5)
+    assert len(kids) == 5
+    for b in mgr.seqs[root].table:
+        assert pool.ref[b] == 6
+    sids = [root] + kids
+    slots, pairs = mgr.append_batch(sids)
+    assert slots.dtype == np.int64 and pairs.shape == (5, 2)
+    # every write lands in an unshared block, distinct per sequence
+    assert len(set(slots.tolist())) == 6
+    for s in slots:
+        assert pool.ref[s // 4] == 1
+    # copies read the shared partial block into fresh blocks
+    src = set(pairs[:, 0].tolist())
+    assert len(src) == 1 and not (src & set(pairs[:, 1].tolist()))
+    assert np.array_equal(mgr.table_refs(), pool.ref)
+    # the next append of every sequence needs no copy
+    _, pairs2 = mgr.append_batch(sids)
+    assert pairs2.shape == (0, 2)
+    assert mgr.fork_many(root, 0) == []

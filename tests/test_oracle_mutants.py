@@ -43,7 +43,21 @@ def _reads_whole_last_block(cache, table_row, kv_head, start, stop, bs, dtype,
     return rows + 0.0 * ora.to_f64(tail, dtype).sum()
 
 
+def _copy_k_only(k_cache, v_cache, block_pairs):
+    kc = np.array(k_cache, copy=True)
+    for src, dst in block_pairs:
+        if src >= 0 and dst >= 0:
+            kc[dst] = kc[src]
+    return kc, np.array(v_cache, copy=True)
+
+
+def _copy_swapped(k_cache, v_cache, block_pairs, _orig=ora.copy_blocks):
+    return _orig(k_cache, v_cache, [(d, s) for s, d in block_pairs])
+
+
 MUTANTS = {
+    "cow_copies_k_only": ("copy_blocks", _copy_k_only),
+    "cow_src_dst_swapped": ("copy_blocks", _copy_swapped),
     "offset_off_by_one": ("physical_slot", _wrong_offset),
     "bf16_decode_shift": ("to_f64", _bf16_bad_shift),
     "gqa_interleaved": ("kv_head_of", _interleaved_heads),
@@ -62,6 +76,8 @@ PIN_CHECKS = [
     pins.test_gqa_mapping_contiguous_groups,
     pins.test_poison_in_unread_slots_does_not_leak,
     pins.test_bf16_storage_path_equals_upcast_f32,
+    pins.test_copy_blocks_bytes_and_untouched_blocks,
+    pins.test_copy_on_write_flow_equals_private_copies,
 ]
 
 
