@@ -214,6 +214,59 @@ def paged_attn_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     return out
 
 
+def query_context_len(L: int, num_query_tokens: int, j: int) -> int:
+    """Positions attended by query token ``j`` of ``num_query_tokens`` new
+    tokens of a sequence whose cache holds ``L`` tokens.
+
+    Reading taken (the pages describe one query per step; several queries per
+    sequence arise from parallel sampling, beam search and draft
+    verification, "PagedAttention核心思想" section 2.4.3): the new tokens are
+    the last ``num_query_tokens`` positions of the sequence, already written to
+    the cache, and each attends to every position up to and including its own,
+    so query ``j`` sees ``[0, L - num_query_tokens + j + 1)``; a query with no
+    such position gets the empty (zero) output.
+    """
+    return max(0, L - num_query_tokens + j + 1)
+
+
+def paged_attn_decode_multi(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                            block_tables: np.ndarray, context_lens: np.ndarray,
+                            block_size: int, scale: float, dtype: str,
+                            triples: Optional[Iterable[Tuple[int, int, int]]] = None,
+                            chunk_tokens: int = 1 << 16):
+    """Decode attention with several query tokens per sequence, in float64.
+
+    ``q`` is [num_seqs, num_query_tokens, num_q_heads, head_dim]; query token
+    ``j`` of sequence ``i`` is ordinary softmax attention over the logical
+    positions ``query_context_len(L_i, T, j)`` walks, read block by block
+    through the sequence's table ("PagedAttention核心思想" section 2.5).
+    ``triples`` optionally restricts the work to (seq, query token, q head)
+    outputs (the others are NaN).  Returns float64 of q's shape.
+    """
+    S, T, Hq, D = q.shape
+    NB, Hkv, BS, D2 = k_cache.shape
+    if BS != block_size or D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape does not match q / block_size")
+    if Hq % Hkv != 0:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    qf = to_f64(q, dtype)
+    if triples is None:
+        triples = [(i, j, h) for i in range(S) for j in range(T) for h in range(Hq)]
+        out = np.zeros((S, T, Hq, D), dtype=np.float64)
+    else:
+        triples = list(triples)
+        out = np.full((S, T, Hq, D), np.nan, dtype=np.float64)
+    for i, j, h in triples:
+        L = int(context_lens[i])
+        if L < 0:
+            raise ValueError("negative context length")
+        o, _ = _attend_one(qf[i, j, h], k_cache, v_cache, np.asarray(block_tables[i]),
+                           kv_head_of(h, Hq, Hkv), query_context_len(L, T, j), block_size,
+                           float(scale), dtype, chunk_tokens, False)
+        out[i, j, h] = o
+    return out
+
+
 # ---------------------------------------------------------------------------
 # KV append (scatter of new tokens into their slots)
 # ---------------------------------------------------------------------------
@@ -270,4 +323,5 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, block_pairs):
 
 
 __all__ = ["DTYPES", "to_f64", "physical_slot", "gather_rows", "kv_head_of",
-           "softmax_weights", "paged_attn_decode", "paged_kv_write", "copy_blocks"]
+           "softmax_weights", "paged_attn_decode", "query_context_len",
+           "paged_attn_decode_multi", "paged_kv_write", "copy_blocks"]

@@ -438,3 +438,90 @@ def test_copy_on_write_flow_equals_private_copies():
         got_v = np.stack([vc[table[t // BS], :, t % BS] for t in range(L)])
         assert np.array_equal(got_k, np.concatenate([prefix_k, new_k[i:i + 1]]))
         assert np.array_equal(got_v, np.concatenate([prefix_v, new_v[i:i + 1]]))
+
+
+# ---------------------------------------------------------------------------
+# several query tokens per sequence (causal among the new tokens)
+# ---------------------------------------------------------------------------
+
+def _multi_problem(rng, lens, T, Hq, Hkv, D, bs, num_blocks):
+    q = rng.standard_normal((len(lens), T, Hq, D))
+    lk = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    lv = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    kp, vp, tables = page_in(lk, lv, lens, bs, num_blocks, rng.permutation(num_blocks))
+    return _f32(q), [to_f64(_f32(x), "f32") for x in lk], [to_f64(_f32(x), "f32") for x in lv], \
+        _f32(kp), _f32(vp), tables
+
+
+@pytest.mark.parametrize("T,Hq,Hkv", [(1, 4, 4), (3, 8, 2), (4, 8, 1), (6, 2, 2)])
+def test_multi_equals_dense_causal_sdpa(T, Hq, Hkv):
+    """Library routine on the logical arrays: torch's attention with an
+    explicit boolean mask, query j allowed positions t <= L - T + j."""
+    from oracle import paged_attn_decode_multi
+    rng = np.random.default_rng(60 + T)
+    lens = [T, 9, 37, 70]
+    D, bs = 8, 4
+    q, lk, lv, kp, vp, tables = _multi_problem(rng, lens, T, Hq, Hkv, D, bs, 64)
+    got = paged_attn_decode_multi(q, kp, vp, tables, np.array(lens), bs, 0.3, "f32")
+    G = Hq // Hkv
+    for i, L in enumerate(lens):
+        K = torch.from_numpy(lk[i]).permute(1, 0, 2).repeat_interleave(G, dim=0)   # [Hq, L, D]
+        V = torch.from_numpy(lv[i]).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        Q = torch.from_numpy(to_f64(q[i], "f32")).permute(1, 0, 2)                  # [Hq, T, D]
+        mask = torch.arange(L)[None, :] <= (L - T + torch.arange(T))[:, None]       # [T, L]
+        o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=0.3)
+        np.testing.assert_allclose(got[i], o.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_multi_brute_force_tiny():
+    from oracle import paged_attn_decode_multi
+    rng = np.random.default_rng(61)
+    lens, T, Hq, Hkv, D = [3, 11, 20], 3, 4, 2, 5
+    q, lk, lv, kp, vp, tables = _multi_problem(rng, lens, T, Hq, Hkv, D, 4, 20)
+    got = paged_attn_decode_multi(q, kp, vp, tables, np.array(lens), 4, 0.45, "f32")
+    qf = to_f64(q, "f32")
+    for i, L in enumerate(lens):
+        for j in range(T):
+            n = L - T + j + 1
+            want = brute_force_decode([qf[i, j].tolist()], [lk[i][:n].tolist()], [lv[i][:n].tolist()],
+                                      0.45, Hq // Hkv)
+            np.testing.assert_allclose(got[i, j], want[0], rtol=1e-12, atol=1e-14)
+
+
+def test_multi_query_j_is_single_decode_at_its_length():
+    """Query j is the one-query decode of a context shortened by T-1-j."""
+    from oracle import paged_attn_decode_multi
+    rng = np.random.default_rng(62)
+    lens, T = np.array([4, 16, 33, 50]), 4
+    q, lk, lv, kp, vp, tables = _multi_problem(rng, list(lens), T, 4, 2, 8, 16, 16)
+    got = paged_attn_decode_multi(q, kp, vp, tables, lens, 16, 0.2, "f32")
+    for j in range(T):
+        want = paged_attn_decode(q[:, j], kp, vp, tables, lens - (T - 1 - j), 16, 0.2, "f32")
+        assert np.array_equal(got[:, j], want)
+
+
+def test_multi_is_causal_among_new_tokens():
+    """Changing a later new token leaves earlier queries bitwise unchanged and
+    changes the queries that see it."""
+    from oracle import paged_attn_decode_multi
+    rng = np.random.default_rng(63)
+    lens, T, bs = [24], 4, 8
+    q, lk, lv, kp, vp, tables = _multi_problem(rng, lens, T, 2, 1, 8, bs, 8)
+    base = paged_attn_decode_multi(q, kp, vp, tables, np.array(lens), bs, 0.5, "f32")
+    t = lens[0] - 2                    # position of new token j = 2
+    b, o = int(tables[0, t // bs]), t % bs
+    kp2, vp2 = kp.copy(), vp.copy()
+    kp2[b, 0, o] += 1.0
+    vp2[b, 0, o] -= 2.0
+    moved = paged_attn_decode_multi(q, kp2, vp2, tables, np.array(lens), bs, 0.5, "f32")
+    assert np.array_equal(moved[0, :2], base[0, :2])
+    assert not np.any(np.isclose(moved[0, 2:], base[0, 2:], rtol=0, atol=1e-9).all(axis=-1))
+
+
+def test_multi_context_shorter_than_queries_gives_zeros():
+    from oracle import paged_attn_decode_multi
+    rng = np.random.default_rng(64)
+    q, lk, lv, kp, vp, tables = _multi_problem(rng, [2], 2, 2, 2, 4, 4, 4)
+    out = paged_attn_decode_multi(np.concatenate([q, q], axis=1), kp, vp, tables, np.array([2]), 4, 1.0, "f32")
+    assert np.all(out[0, :2] == 0.0)
+    assert np.array_equal(out[0, 2:], paged_attn_decode_multi(q, kp, vp, tables, np.array([2]), 4, 1.0, "f32")[0])

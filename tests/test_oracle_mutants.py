@@ -55,7 +55,17 @@ def _copy_swapped(k_cache, v_cache, block_pairs, _orig=ora.copy_blocks):
     return _orig(k_cache, v_cache, [(d, s) for s, d in block_pairs])
 
 
+def _causal_off_by_one(L, T, j):
+    return max(0, L - T + j)
+
+
+def _not_causal(L, T, j):
+    return max(0, L)
+
+
 MUTANTS = {
+    "multi_mask_off_by_one": ("query_context_len", _causal_off_by_one),
+    "multi_not_causal": ("query_context_len", _not_causal),
     "cow_copies_k_only": ("copy_blocks", _copy_k_only),
     "cow_src_dst_swapped": ("copy_blocks", _copy_swapped),
     "offset_off_by_one": ("physical_slot", _wrong_offset),
@@ -78,6 +88,9 @@ PIN_CHECKS = [
     pins.test_bf16_storage_path_equals_upcast_f32,
     pins.test_copy_blocks_bytes_and_untouched_blocks,
     pins.test_copy_on_write_flow_equals_private_copies,
+    lambda: pins.test_multi_equals_dense_causal_sdpa(3, 8, 2),
+    pins.test_multi_brute_force_tiny,
+    pins.test_multi_is_causal_among_new_tokens,
 ]
 
 
