@@ -200,6 +200,82 @@ int paged_decode_step(void *out, const void *q, const void *k_new, const void *v
                       float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/*
+ * paged_attn_decode_multi -- several query tokens per sequence.
+ *
+ * Parallel sampling, beam search and the verification of drafted tokens give
+ * a sequence more than one query in a step ("PagedAttention核心思想" section
+ * 2.4.3).  The T = num_query_tokens new tokens of sequence i are its last T
+ * positions, already written to the cache (paged_kv_write), and each attends
+ * to every position up to and including its own:
+ *   out[i,j,h,:] = sum_t softmax(s)_t * V_t,  t in [0, L_i - T + j + 1),
+ * with s as for paged_attn_decode; a query whose window is empty (L_i < T - j)
+ * gets zeros.  The cache is read block by block through the table exactly as
+ * for one query ("PagedAttention核心思想" section 2.5).
+ *
+ *   out, q        [num_seqs, num_query_tokens, num_q_heads, head_dim], 16-byte
+ *                 aligned, dtype of the caches
+ *   dtype         PKV_F16 or PKV_BF16 (PKV_F32: PKV_ERR_UNSUPPORTED); products
+ *                 run on matrix cores with fp32 accumulation; the softmax
+ *                 weights multiply V as fp16 (11 significant bits) or as a
+ *                 bf16 head plus a bf16 remainder (about 16 bits)
+ *   head_dim      64 or 128; block_size a power of two from 16 to 256; any
+ *                 num_q_heads / num_kv_heads
+ *   workspace     >= paged_attn_decode_multi_workspace_size(...) bytes,
+ *                 256-byte aligned, first PKV_DECODE_COUNTER_BYTES zero once
+ *                 (every call leaves them zero; same contract as
+ *                 paged_attn_decode)
+ * Other arguments, preconditions and errors as for paged_attn_decode.
+ */
+size_t paged_attn_decode_multi_workspace_size(int32_t num_seqs, int32_t num_query_tokens,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim);
+int paged_attn_decode_multi(void *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t max_blocks_per_seq, int64_t num_blocks,
+                            int32_t max_context_len, float scale, int32_t dtype,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attn_decode_shared -- one query per sequence, with the shared prefix
+ * of forked sequences read once for the whole group.
+ *
+ * Forks of one request (parallel sampling, beam search) point their Block
+ * Tables at the same physical blocks for the prompt they share
+ * ("PagedAttention核心思想" section 2.4.3; "PagedAttention技术解析" section 2.1).
+ * The result is exactly paged_attn_decode's; the sharing only changes how
+ * often those blocks are read: the prefix of every group is streamed once for
+ * all query heads of all its members, each member then streams its own
+ * suffix, and the two partial softmax results are merged.
+ *
+ *   group_starts  int32 [num_groups + 1] on the device: the members of group g
+ *                 are sequences group_starts[g] .. group_starts[g+1] - 1
+ *                 (consecutive; group_starts[0] = 0, group_starts[num_groups]
+ *                 = num_seqs, non-decreasing)
+ *   prefix_lens   int32 [num_seqs] on the device: P_i, the leading positions
+ *                 sequence i shares with its group (0 for none)
+ * Preconditions (device data, not checked): within a group P_i is the same,
+ * P_i <= L_i, and block_tables[i][j] is the same physical block for every
+ * member and every j < ceil(P_i / block_size).
+ *   workspace     >= paged_attn_decode_shared_workspace_size(...) bytes; same
+ *                 contract as paged_attn_decode_multi
+ * Two launches on `stream`; other arguments and errors as for
+ * paged_attn_decode_multi.
+ */
+size_t paged_attn_decode_shared_workspace_size(int32_t num_seqs, int32_t num_groups,
+                                               int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim);
+int paged_attn_decode_shared(void *out, const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, const int32_t *context_lens,
+                             const int32_t *group_starts, const int32_t *prefix_lens,
+                             int32_t num_seqs, int32_t num_groups, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_context_len, float scale, int32_t dtype,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

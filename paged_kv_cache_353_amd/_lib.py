@@ -72,6 +72,18 @@ def load_library() -> ctypes.CDLL:
         lib.paged_decode_step.restype = c_int
         lib.paged_copy_blocks.argtypes = [c_p, c_p, c_p, c_i64, c_i32, c_i32, c_i32, c_i64, c_i32, c_p]
         lib.paged_copy_blocks.restype = c_int
+        lib.paged_attn_decode_multi_workspace_size.argtypes = [c_i32] * 5
+        lib.paged_attn_decode_multi_workspace_size.restype = c_sz
+        lib.paged_attn_decode_multi.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32,
+                                                c_i32, c_i32, c_i32, c_i32, c_i64, c_i32, c_f,
+                                                c_i32, c_p, c_sz, c_p]
+        lib.paged_attn_decode_multi.restype = c_int
+        lib.paged_attn_decode_shared_workspace_size.argtypes = [c_i32] * 5
+        lib.paged_attn_decode_shared_workspace_size.restype = c_sz
+        lib.paged_attn_decode_shared.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i32,
+                                                 c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i64,
+                                                 c_i32, c_f, c_i32, c_p, c_sz, c_p]
+        lib.paged_attn_decode_shared.restype = c_int
         _lib = lib
         return lib
 
@@ -235,4 +247,109 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
             int(max_context_len), float(scale), _dtype_code(q),
             workspace.data_ptr() if workspace.numel() else None, workspace.numel(),
             _stream_handle(q.device)))
+    return out
+
+
+def _check_cache_args(k_cache, v_cache, block_tables, context_lens, num_seqs, dtype, block_size):
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if k_cache.dtype != dtype or v_cache.dtype != dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs or context_lens.shape != (num_seqs,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
+    for t in (k_cache, v_cache, block_tables, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if int(block_size) != k_cache.shape[2]:
+        raise ValueError("block_size must equal k_cache.shape[2]")
+
+
+def paged_attn_decode_multi_workspace_size(num_seqs: int, num_query_tokens: int, num_q_heads: int,
+                                           num_kv_heads: int, head_dim: int) -> int:
+    lib = load_library()
+    return int(lib.paged_attn_decode_multi_workspace_size(num_seqs, num_query_tokens, num_q_heads,
+                                                          num_kv_heads, head_dim))
+
+
+def paged_attn_decode_multi(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, block_size: int, scale: float,
+                            max_context_len: Optional[int] = None,
+                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Several query tokens per sequence: ``q``/``out`` are
+    [num_seqs, num_query_tokens, num_q_heads, head_dim]; query token ``j`` of
+    sequence ``i`` sits at position ``L_i - T + j`` (already in the cache) and
+    attends to ``[0, L_i - T + j + 1)``.  fp16/bf16 only.  Other arguments and
+    the workspace contract as for ``paged_attn_decode``.  Returns ``out``."""
+    if q.dim() != 4 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [num_seqs, num_query_tokens, num_q_heads, head_dim]")
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("all tensors must be contiguous")
+    S, T, hq, d = q.shape
+    _check_cache_args(k_cache, v_cache, block_tables, context_lens, S, q.dtype, block_size)
+    nb, hkv, bs, _ = k_cache.shape
+    mb = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mb * bs
+    lib = load_library()
+    need = int(lib.paged_attn_decode_multi_workspace_size(S, T, hq, hkv, d))
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.paged_attn_decode_multi(
+            out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), S, T, hq, hkv, d, bs, mb, nb,
+            int(max_context_len), float(scale), _dtype_code(q),
+            workspace.data_ptr() if workspace.numel() else None, workspace.numel(),
+            _stream_handle(q.device)))
+    return out
+
+
+def paged_attn_decode_shared_workspace_size(num_seqs: int, num_groups: int, num_q_heads: int,
+                                            num_kv_heads: int, head_dim: int) -> int:
+    lib = load_library()
+    return int(lib.paged_attn_decode_shared_workspace_size(num_seqs, num_groups, num_q_heads,
+                                                           num_kv_heads, head_dim))
+
+
+def paged_attn_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                             v_cache: torch.Tensor, block_tables: torch.Tensor,
+                             context_lens: torch.Tensor, group_starts: torch.Tensor,
+                             prefix_lens: torch.Tensor, block_size: int, scale: float,
+                             max_context_len: Optional[int] = None,
+                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One query per sequence, reading each group's shared prefix once.
+
+    ``group_starts`` int32 [num_groups + 1] and ``prefix_lens`` int32
+    [num_seqs], both on the device: the members of group ``g`` are sequences
+    ``group_starts[g] .. group_starts[g+1] - 1``, and their tables share the
+    blocks of the first ``prefix_lens[i]`` positions (see
+    ``sharing.shared_prefix_groups``).  The result equals ``paged_attn_decode``.
+    fp16/bf16 only.  Returns ``out``."""
+    _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, block_size)
+    S, hq, d = q.shape
+    if group_starts.dtype != torch.int32 or prefix_lens.dtype != torch.int32:
+        raise TypeError("group_starts and prefix_lens must be int32")
+    if group_starts.dim() != 1 or group_starts.shape[0] < 2 or prefix_lens.shape != (S,):
+        raise ValueError("group_starts must be [num_groups + 1] and prefix_lens [num_seqs]")
+    if not (group_starts.is_contiguous() and prefix_lens.is_contiguous()):
+        raise ValueError("all tensors must be contiguous")
+    ng = group_starts.shape[0] - 1
+    nb, hkv, bs, _ = k_cache.shape
+    mb = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mb * bs
+    lib = load_library()
+    need = int(lib.paged_attn_decode_shared_workspace_size(S, ng, hq, hkv, d))
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.paged_attn_decode_shared(
+            out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), group_starts.data_ptr(),
+            prefix_lens.data_ptr(), S, ng, hq, hkv, d, bs, mb, nb, int(max_context_len),
+            float(scale), _dtype_code(q), workspace.data_ptr() if workspace.numel() else None,
+            workspace.numel(), _stream_handle(q.device)))
     return out

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 
-SOURCES = ["kv_write.hip", "attn_decode.hip", "pkv_api.cpp"]
+SOURCES = ["kv_write.hip", "attn_decode.hip", "attn_multi.hip", "pkv_api.cpp"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -1,0 +1,656 @@
+// Paged decode attention with many query columns per KV head, for gfx950.
+//
+// Two extensions of the single-query decode share this kernel:
+//  * several query tokens per sequence (parallel sampling, beam search and
+//    draft verification produce them), each attending to every position up
+//    to its own: the new tokens are the last T positions of the sequence;
+//  * forks whose Block Tables point at the same physical blocks for a common
+//    prefix ("PagedAttention核心思想" section 2.4.3): the prefix is streamed
+//    once for all forks of a group, then each fork streams its own suffix and
+//    the two partial results are merged.
+// Either way one K/V tile serves up to 16 query columns, which turns both
+// products of the tile into matrix-core work:
+//  * scores S = K q^T: one 16x16x32 MFMA per 32 dims, tokens as rows and
+//    query columns as columns (lane (r, j) receives tokens 4r..4r+3 of
+//    column j);
+//  * output O^T += V^T P: one 16x16x16 MFMA per 16 output dims (two for
+//    bfloat16, whose probabilities go in as head + remainder).  The B
+//    operand (16 tokens x 16 columns) is exactly the score layout, rounded to
+//    the cache's 16-bit type; the A operand (16 dims x 16 tokens) is taken
+//    from V rows 4r..4r+3 that lane (r, c) loaded, dims c*DL..c*DL+DL-1, by
+//    pairing the same element of the four rows.  Lane (r, j) ends up owning
+//    dims [r*D/4, (r+1)*D/4) of column j.
+// Softmax keeps one running (max, exp-sum) per column; a tile's column max
+// takes two lane exchanges across the row groups.
+//
+// Work split, masking and merging follow the single-query kernel: every
+// (row, KV head, column chunk) unit is cut into 16-token sub-tiles, all
+// sub-tiles are shared out in equal contiguous ranges, one per resident
+// wave; a unit split between k waves leaves k partial records that the last
+// arriver merges in a fixed order (two levels for large k).  Loads use
+// descriptors that span only the unit's valid rows, so rows past the end read
+// as zero, and every score outside a column's window is set to -inf before the
+// exponential, so stale cache contents never reach the result.
+#include "pkv_device.h"
+
+#include <atomic>
+
+namespace pkv {
+namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMDirectMerge = 8;  // units split in at most this many pieces merge in one level
+constexpr int kMDepth = 2;        // sub-tiles in flight per wave
+
+// Position of a wave's load or compute stage.  Every field is wave-uniform.
+struct MCursor {
+    int row;     // sequence, or group in the prefix mode
+    int kvh;     // KV head
+    int chunk;   // column chunk
+    int sub;     // sub-tile inside the unit
+    int n;       // sub-tiles of every unit of the row
+    int chunks;  // column chunks of the row
+    int t0;      // position of the row's first sub-tile (a multiple of 16)
+    int tend;    // one past the row's last position read
+    int lo;      // first position any column of the row attends
+    int L;       // the row's sequence length (multi mode: the query window's end)
+    int tseq;    // sequence whose Block Table the row walks
+    int cols;    // query columns of the row, per KV head
+    int pre;     // sub-tiles of all rows before this one
+    int upre;    // units of all rows before this one
+};
+
+// O^T += V^T P on one 16-dim slice: A = 4 tokens x 1 dim per lane (as four
+// 16-bit values), B = the 4 probabilities of this lane's column.
+template <typename DT>
+__device__ __forceinline__ f32x4 mfma_pv(u32x2 a, u32x2 b, f32x4 c) {
+    if constexpr (std::is_same_v<DT, BF16>) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                         __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    }
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Four probabilities as the B operand.  fp16 keeps 11 significant bits,
+// enough for the output tolerance.  bfloat16 keeps 8, too few where a handful
+// of tokens carry the weight, so each probability is split into a rounded
+// head and the rounded remainder, and both multiply V (two MFMAs): together
+// they carry about 16 significant bits.
+__device__ __forceinline__ u32x2 pack_probs_f16(const float (&p)[4]) {
+    f16x2 a, b;
+    a[0] = (_Float16)p[0];
+    a[1] = (_Float16)p[1];
+    b[0] = (_Float16)p[2];
+    b[1] = (_Float16)p[3];
+    return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+__device__ __forceinline__ uint32_t cvt2_bf16(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+}
+__device__ __forceinline__ void split_probs_bf16(const float (&p)[4], u32x2 &hi, u32x2 &lo) {
+    hi = u32x2{cvt2_bf16(p[0], p[1]), cvt2_bf16(p[2], p[3])};
+    float r[4];
+    static_for<0, 2>([&]<int k>() {
+        r[2 * k] = p[2 * k] - as_f(hi[k] << 16);
+        r[2 * k + 1] = p[2 * k + 1] - as_f(hi[k] & 0xFFFF0000u);
+    });
+    lo = u32x2{cvt2_bf16(r[0], r[1]), cvt2_bf16(r[2], r[3])};
+}
+
+// 16-bit element E of a lane's slice of a V row (dword E/2, half E%2).
+template <int E, typename VR>
+__device__ __forceinline__ uint32_t v_half(const VR &v) {
+    const uint32_t w = v[E / 2];
+    return (E & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+template <typename DT, int D>
+__global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(MultiArgs a) {
+    constexpr int EB = DT::kBytes;
+    static_assert(EB == 2, "16-bit caches only");
+    constexpr int ROW = D * EB;      // bytes per token row
+    constexpr int NLK = D / 32;      // 16-byte K loads per lane per sub-tile (one per 32-dim MFMA step)
+    constexpr int DL = D / 16;       // dims of a V row per lane (and 16x16x16 MFMAs per sub-tile)
+    constexpr int DQ = D / 4;        // output dims owned by a lane
+    typedef typename std::conditional<DL == 8, u32x4, u32x2>::type VReg;
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int rg = lane >> 4;   // row group: tokens 4rg..4rg+3 of a sub-tile
+    const int c = lane & 15;    // column (scores, output) / token row (K) / dim slice (V)
+    const int wave = uniform((int)blockIdx.x * kWavesPerGroup + (int)(threadIdx.x >> 6));
+    const int R = a.num_rows, Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+    const int G = Hq / Hkv;
+    const int Tq = a.num_query_tokens;
+    const int Lmax = a.max_context_len;
+    const int W = a.num_waves;
+    const int mode = a.mode;
+    auto clampL = [&](int L) { L = L < Lmax ? L : Lmax; return L > 0 ? L : 0; };
+
+    // ---- row description; `ld` reads a 32-bit entry of a length array
+    struct RowInfo { int t0, tend, lo, L, tseq, cols; };
+    auto row_info = [&](int r, auto ld) -> RowInfo {
+        RowInfo ri{};
+        if (mode == kModePrefix) {
+            // members clamped to the batch (the description is device data)
+            int f = ld(a.group_starts, r), e = ld(a.group_starts, r + 1);
+            f = min(max(f, 0), a.num_seqs);
+            e = min(max(e, f), a.num_seqs);
+            const int P = clampL(ld(a.prefix_lens, f));
+            ri.t0 = 0; ri.tend = P; ri.lo = 0; ri.L = P; ri.tseq = f; ri.cols = (e - f) * G;
+        } else if (mode == kModeSuffix) {
+            const int L = clampL(ld(a.context_lens, r));
+            int P = clampL(ld(a.prefix_lens, r));
+            P = P < L ? P : L;
+            // an empty suffix streams nothing (its output is the prefix record)
+            ri.t0 = P < L ? (P & ~15) : P; ri.tend = L; ri.lo = P; ri.L = L; ri.tseq = r; ri.cols = G;
+        } else {
+            const int L = clampL(ld(a.context_lens, r));
+            ri.t0 = 0; ri.tend = L; ri.lo = 0; ri.L = L; ri.tseq = r; ri.cols = Tq * G;
+        }
+        return ri;
+    };
+    auto ld_vec = [](const int32_t *p, int i) { return p[i]; };
+    auto ld_scalar = [](const int32_t *p, int i) { return ((const_i32_ptr)p)[i]; };
+    auto tiles_of = [&](const RowInfo &ri) { return (ri.tend - ri.t0 + 15) >> 4; };
+    auto chunks_of = [&](const RowInfo &ri) { return (ri.cols + kMultiCols - 1) / kMultiCols; };
+
+    // ---- rows with nothing to stream: zero outputs, or (suffix mode) the
+    // prefix record on its own
+    if (mode != kModePrefix) {
+        for (int r = wave; r < R; r += W) {
+            const RowInfo ri = row_info(r, ld_scalar);
+            if (ri.tend - ri.t0 > 0) continue;
+            // here L == 0 (multi) or the suffix is empty (suffix mode)
+            const int nrow = mode == kModeMulti ? Tq * Hq : Hq;
+            char *o = static_cast<char *>(a.out) + (int64_t)r * nrow * ROW;
+            for (int idx = lane; idx < nrow * (ROW / 16); idx += kWave) {
+                const int h = idx / (ROW / 16), ch = idx - h * (ROW / 16);
+                u32x4 z = {0u, 0u, 0u, 0u};
+                if (mode == kModeSuffix && ri.lo > 0) {
+                    const int64_t rec = (int64_t)r * Hq + h;
+                    const float l = a.pre_ml[2 * rec + 1];
+                    const float inv = l > 0.f ? 1.f / l : 0.f;
+                    float f[8];
+                    for (int e = 0; e < 8; ++e) f[e] = a.pre_acc[rec * D + ch * 8 + e] * inv;
+                    z = pack_chunk<DT>(f);
+                }
+                *reinterpret_cast<u32x4 *>(o + (int64_t)h * ROW + ch * 16) = z;
+            }
+        }
+    }
+
+    // ---- total work and this wave's range
+    int N = 0, U = 0;
+    for (int base = 0; base < R; base += kWave) {
+        const int r = base + lane;
+        if (r < R) {
+            const RowInfo ri = row_info(r, ld_vec);
+            const int n = tiles_of(ri);
+            N += Hkv * chunks_of(ri) * n;
+            U += n > 0 ? Hkv * chunks_of(ri) : 0;
+        }
+    }
+    const int T = uniform(wave_sum_i(N, lane));
+    // a group description that breaks its preconditions (overlapping groups)
+    // could ask for more units than the workspace holds: do nothing then
+    if (uniform(wave_sum_i(U, lane)) > a.max_units) return;
+    const int Weff = T < W ? T : W;
+    if (wave >= Weff) return;
+    auto start_of = [&](int w) -> int { return (int)((int64_t)T * w / Weff); };
+    auto wave_of = [&](int x) -> int {  // the largest w with start_of(w) <= x
+        int w = (int)(((int64_t)x * Weff) / T);
+        w = min(max(w, 0), Weff - 1);
+        while (w + 1 < Weff && start_of(w + 1) <= x) ++w;
+        while (w > 0 && start_of(w) > x) --w;
+        return w;
+    };
+    const int g0 = start_of(wave);
+    const int g1 = start_of(wave + 1);
+
+    auto load_row = [&](MCursor &u) {
+        const RowInfo ri = row_info(u.row, ld_scalar);
+        u.t0 = uniform(ri.t0); u.tend = uniform(ri.tend); u.lo = uniform(ri.lo); u.L = uniform(ri.L);
+        u.tseq = uniform(ri.tseq); u.cols = uniform(ri.cols);
+        u.n = uniform((u.tend - u.t0 + 15) >> 4);
+        u.chunks = uniform((u.cols + kMultiCols - 1) / kMultiCols);
+    };
+
+    // ---- locate g0: row (prefix scans of sub-tiles and units), then unit and sub-tile
+    MCursor cur{};
+    {
+        int pre = 0, upre = 0;
+        for (int base = 0; base < R; base += kWave) {
+            const int r = base + lane;
+            int tl = 0, un = 0;
+            if (r < R) {
+                const RowInfo ri = row_info(r, ld_vec);
+                const int n = tiles_of(ri);
+                un = n > 0 ? Hkv * chunks_of(ri) : 0;
+                tl = un * n;
+            }
+            const int incl = wave_incl_scan(tl, lane);
+            const int uincl = wave_incl_scan(un, lane);
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(pre + incl > g0);
+            if (hit) {
+                const int f = __builtin_ctzll(hit);
+                cur.row = base + f;
+                cur.pre = pre + __builtin_amdgcn_readlane(incl - tl, f);
+                cur.upre = upre + __builtin_amdgcn_readlane(uincl - un, f);
+                break;
+            }
+            pre += __builtin_amdgcn_readlane(incl, kWave - 1);
+            upre += __builtin_amdgcn_readlane(uincl, kWave - 1);
+        }
+        cur.row = uniform(cur.row);
+        cur.pre = uniform(cur.pre);
+        cur.upre = uniform(cur.upre);
+        load_row(cur);
+        const int rem = g0 - cur.pre;
+        const int uir = rem / cur.n;
+        cur.sub = rem - uir * cur.n;
+        cur.kvh = uir / cur.chunks;
+        cur.chunk = uir - cur.kvh * cur.chunks;
+    }
+    auto advance = [&](MCursor &u) {
+        if (++u.sub < u.n) return;
+        u.sub = 0;
+        if (++u.chunk < u.chunks) return;
+        u.chunk = 0;
+        if (++u.kvh < Hkv) return;
+        u.kvh = 0;
+        u.pre += Hkv * u.chunks * u.n;
+        u.upre += Hkv * u.chunks;
+        do {
+            ++u.row;
+            load_row(u);
+        } while (u.n == 0 && u.row + 1 < R);
+    };
+    auto unit_index = [&](const MCursor &u) { return u.upre + u.kvh * u.chunks + u.chunk; };
+    auto unit_first = [&](const MCursor &u) { return u.pre + (u.kvh * u.chunks + u.chunk) * u.n; };
+
+    const char *kc = static_cast<const char *>(a.k_cache);
+    const char *vc = static_cast<const char *>(a.v_cache);
+    const int BS = 1 << a.block_shift;
+    const int64_t head_bytes = (int64_t)BS * ROW;
+    const int64_t block_bytes = (int64_t)Hkv * head_bytes;
+    const int koff = c * ROW + 16 * rg;              // K: token c, dims 32b + 8rg ..
+    const int voff = 4 * rg * ROW + c * DL * EB;     // V: tokens 4rg + m, dims c*DL ..
+
+    auto issue = [&](const MCursor &u, bool live, u32x4 (&kr)[NLK], VReg (&vr)[4]) {
+        const int tok = u.t0 + (u.sub << 4);
+        const int j = tok >> a.block_shift;
+        const int row0 = tok - (j << a.block_shift);
+        int rows = u.tend - tok;
+        rows = rows < 16 ? rows : 16;
+        rows = live ? rows : 0;
+        const const_i32_ptr table = (const_i32_ptr)(a.block_tables + (int64_t)u.tseq * a.max_blocks_per_seq);
+        const int64_t phys = table[j];
+        const int64_t off = uniform(phys * block_bytes + (int64_t)u.kvh * head_bytes + (int64_t)row0 * ROW);
+        const int nbytes = uniform(rows * ROW);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kc + off), 0, nbytes, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vc + off), 0, nbytes, kBufferFlags);
+        static_for<0, NLK>([&]<int b>() { kr[b] = load_chunk(rk, koff + 64 * b); });
+        static_for<0, 4>([&]<int m>() {
+            if constexpr (DL == 8) vr[m] = load_chunk(rv, voff + m * ROW);
+            else vr[m] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + m * ROW, 0, 0));
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- per-unit state
+    u32x4 qr[NLK];        // B operand of the scores: column c (zero when absent)
+    int lim = 0;          // this lane's column attends positions [lo, lim)
+    int64_t orow = -1;    // multi/suffix: output row of this lane's column; prefix: record index
+    float m_run = kNegInf, l_run = 0.f;   // lane (rg, c): column c; l_run is this lane's share
+    f32x4 acc[DL];        // acc[e][i]: column c, dim (4rg + i) * DL + e
+    int seg_first = g0;
+
+    auto start_unit = [&](const MCursor &u) {
+        const int x = u.chunk * kMultiCols + c;     // column index within the row
+        const bool valid = x < u.cols;
+        int qrel = 0;                               // q row relative to the row's first q row
+        int64_t qbase = 0;                          // first q row of the row
+        int qspan = 0;                              // q rows of the row
+        if (mode == kModeMulti) {
+            const int jq = x / G, h = x - jq * G;
+            qbase = (int64_t)u.row * Tq * Hq;
+            qspan = Tq * Hq;
+            qrel = jq * Hq + u.kvh * G + h;
+            lim = valid ? u.L - Tq + jq + 1 : 0;
+        } else if (mode == kModePrefix) {
+            const int mem = x / G, h = x - mem * G;
+            qbase = (int64_t)u.tseq * Hq;
+            qspan = (u.cols / G) * Hq;
+            qrel = mem * Hq + u.kvh * G + h;
+            lim = valid ? u.L : 0;
+        } else {
+            qbase = (int64_t)u.row * Hq;
+            qspan = Hq;
+            qrel = u.kvh * G + x;
+            lim = valid ? u.L : 0;
+        }
+        orow = valid ? qbase + qrel : -1;
+        const char *qb = static_cast<const char *>(a.q) + uniform(qbase * ROW);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, uniform(qspan * ROW), kBufferFlags);
+        const int qoff = valid ? qrel * ROW + 16 * rg : 0x7FFFFF00;   // out of range: zero
+        static_for<0, NLK>([&]<int b>() { qr[b] = load_chunk(rq, qoff + 64 * b); });
+#pragma unroll
+        for (int b = 0; b < NLK; ++b) asm volatile("" ::"v"(qr[b]));
+        m_run = kNegInf;
+        l_run = 0.f;
+        static_for<0, DL>([&]<int e>() { acc[e] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+    };
+
+    // One sub-tile: scores, the column-wise online softmax, O^T += V^T P.
+    auto process = [&](const MCursor &u, const u32x4 (&kr)[NLK], const VReg (&vr)[4]) {
+        const int tok = u.t0 + (u.sub << 4) + 4 * rg;
+        const int lo = u.lo;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        static_for<0, NLK>([&]<int b>() { s = mfma_chunk<DT>(kr[b], qr[b], s); });
+        float sv[4];
+        float tmax = kNegInf;
+        static_for<0, 4>([&]<int r>() {
+            const int t = tok + r;
+            sv[r] = (t >= lo && t < lim) ? s[r] * a.scale_log2 : kNegInf;
+            tmax = fmaxf(tmax, sv[r]);
+        });
+        tmax = fmaxf(tmax, xor16(tmax));
+        tmax = fmaxf(tmax, xor32(tmax, lane));
+        const float m_new = fmaxf(m_run, tmax);
+        const float mu = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - mu);
+        float p[4];
+        static_for<0, 4>([&]<int r>() { p[r] = fast_exp2(sv[r] - mu); });
+        l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        m_run = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+            static_for<0, DL>([&]<int e>() { acc[e] *= alpha; });
+        }
+        if constexpr (std::is_same_v<DT, BF16>) {
+            u32x2 ph, pl;
+            split_probs_bf16(p, ph, pl);
+            static_for<0, DL>([&]<int e>() {
+                const u32x2 av = {v_half<e>(vr[0]) | (v_half<e>(vr[1]) << 16),
+                                  v_half<e>(vr[2]) | (v_half<e>(vr[3]) << 16)};
+                acc[e] = mfma_pv<DT>(av, ph, acc[e]);
+                acc[e] = mfma_pv<DT>(av, pl, acc[e]);
+            });
+        } else {
+            const u32x2 pb = pack_probs_f16(p);
+            static_for<0, DL>([&]<int e>() {
+                const u32x2 av = {v_half<e>(vr[0]) | (v_half<e>(vr[1]) << 16),
+                                  v_half<e>(vr[2]) | (v_half<e>(vr[3]) << 16)};
+                acc[e] = mfma_pv<DT>(av, pb, acc[e]);
+            });
+        }
+    };
+
+    // ---- results.  A lane's dims in record / output order: (i, e) -> i * DL + e.
+    auto column_sum = [&](float x) {
+        x += xor16(x);
+        return x + xor32(x, lane);
+    };
+    // Writes (acc / l) for this lane's column, rounded to the output type.
+    auto write_final = [&](const f32x4 (&ac)[DL], float l) {
+        if (orow < 0) return;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        char *o = static_cast<char *>(a.out) + orow * ROW + rg * DQ * EB;
+        static_for<0, 4>([&]<int i>() {
+            float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            static_for<0, DL>([&]<int e>() { f[e] = ac[e][i] * inv; });
+            const u32x4 pk = pack_chunk<DT>(f);
+            if constexpr (DL == 8) *reinterpret_cast<u32x4 *>(o + i * 16) = pk;
+            else *reinterpret_cast<u32x2 *>(o + i * 8) = u32x2{pk[0], pk[1]};
+        });
+    };
+    // Stores a (max, exp-sum, acc) record of this lane's column: acc at
+    // racc + col * D, (max, sum) at rml + 2 * col.
+    auto store_record = [&](float *racc, float *rml, int racc_bytes, int col, float m, float l,
+                            const f32x4 (&ac)[DL], bool coherent) {
+        static_for<0, 4>([&]<int i>() {
+            static_for<0, DL / 4>([&]<int v>() {
+                const f32x4 x = {ac[4 * v][i], ac[4 * v + 1][i], ac[4 * v + 2][i], ac[4 * v + 3][i]};
+                const int off = (col * D + rg * DQ + i * DL + 4 * v) * 4;
+                if (coherent) store_coherent(racc, racc_bytes, off, x);
+                else *reinterpret_cast<f32x4 *>(reinterpret_cast<char *>(racc) + off) = x;
+            });
+        });
+        if (rg == 0) {
+            if (coherent) {
+                __hip_atomic_store(rml + 2 * col, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(rml + 2 * col + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                rml[2 * col] = m;
+                rml[2 * col + 1] = l;
+            }
+        }
+    };
+    // Folds record (m2, l2, a2) into (m, l, ac), in that order.
+    auto fold = [&](float &m, float &l, f32x4 (&ac)[DL], float m2, float l2, const f32x4 (&a2)[DL]) {
+        const float mn = fmaxf(m, m2);
+        const float mu = mn == kNegInf ? 0.f : mn;
+        const float x = fast_exp2(m - mu), y = fast_exp2(m2 - mu);
+        l = l * x + l2 * y;
+        static_for<0, DL>([&]<int e>() {
+            static_for<0, 4>([&]<int i>() { ac[e][i] = __builtin_fmaf(a2[e][i], y, ac[e][i] * x); });
+        });
+        m = mn;
+    };
+    // Loads this lane's part of record `slot` (acc in [i * DL + e] order).
+    auto load_record = [&](const float *racc, const float *rml, int64_t slot, float &m, float &l,
+                           f32x4 (&ac)[DL]) {
+        const float *ra = racc + slot * kMultiCols * D;
+        const float *rm = rml + slot * kMultiCols * 2;
+        static_for<0, 4>([&]<int i>() {
+            static_for<0, DL / 4>([&]<int v>() {
+                const f32x4 x = load_coherent(ra, kMultiCols * D * 4, (c * D + rg * DQ + i * DL + 4 * v) * 4);
+                static_for<0, 4>([&]<int k>() { ac[4 * v + k][i] = x[k]; });
+            });
+        });
+        m = __hip_atomic_load(rm + 2 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        l = __hip_atomic_load(rm + 2 * c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // Merges records [first, first + cnt) in index order.
+    auto merge = [&](const float *racc, const float *rml, int64_t first, int cnt, float &m, float &l,
+                     f32x4 (&ac)[DL]) {
+        load_record(racc, rml, first, m, l, ac);
+        for (int r = 1; r < cnt; ++r) {
+            float m2, l2;
+            f32x4 a2[DL];
+            load_record(racc, rml, first + r, m2, l2, a2);
+            fold(m, l, ac, m2, l2, a2);
+        }
+    };
+    // The unit's result: output (multi), output merged with the prefix
+    // record (suffix), or the prefix record itself (prefix).
+    auto finalize = [&](const MCursor &u, float m, float l, f32x4 (&ac)[DL]) {
+        if (orow < 0) return;
+        if (mode == kModePrefix) {
+            store_record(a.pre_acc + orow * D, a.pre_ml + 2 * orow, 0, 0, m, l, ac, false);
+            return;
+        }
+        if (mode == kModeSuffix && u.lo > 0) {
+            f32x4 a2[DL];
+            const float *pa = a.pre_acc + orow * D + rg * DQ;
+            static_for<0, 4>([&]<int i>() {
+                static_for<0, DL / 4>([&]<int v>() {
+                    const f32x4 x = *reinterpret_cast<const f32x4 *>(pa + i * DL + 4 * v);
+                    static_for<0, 4>([&]<int k>() { a2[4 * v + k][i] = x[k]; });
+                });
+            });
+            fold(m, l, ac, a.pre_ml[2 * orow], a.pre_ml[2 * orow + 1], a2);
+        }
+        write_final(ac, l);
+    };
+
+    auto arrive = [&](int32_t *ctr) {
+        wait_vmem_done();
+        int old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return __builtin_amdgcn_readlane(old, 0);
+    };
+    auto reset = [&](int32_t *ctr) {
+        if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
+    auto finish_unit = [&](const MCursor &u, int g_last) {
+        float l = column_sum(l_run);
+        float m = m_run;
+        const int ua = unit_first(u);
+        const int ub = ua + u.n;
+        if (seg_first == ua && g_last + 1 == ub) {
+            finalize(u, m, l, acc);
+            return;
+        }
+        const int w_first = wave_of(ua);
+        const int w_last = wave_of(ub - 1);
+        const int k = w_last - w_first + 1;
+        const int unit = unit_index(u);
+        const int64_t base = (int64_t)w_first + unit;
+        const int64_t slot = (int64_t)wave + unit;
+        store_record(a.ws_acc + slot * kMultiCols * D, a.ws_ml + slot * kMultiCols * 2, kMultiCols * D * 4, c,
+                     m, l, acc, true);
+        f32x4 ac[DL];
+        if (k <= kMDirectMerge) {
+            if (arrive(a.ws_cnt + unit) != k - 1) return;
+            merge(a.ws_acc, a.ws_ml, base, k, m, l, ac);
+            finalize(u, m, l, ac);
+            reset(a.ws_cnt + unit);
+            return;
+        }
+        int f1 = (int)__builtin_sqrtf((float)k);
+        while (f1 * f1 < k) ++f1;
+        const int ng = (k + f1 - 1) / f1;
+        const int r = wave - w_first;
+        const int j = r / f1;
+        const int kj = min(f1, k - j * f1);
+        const int64_t gslot = base + j;
+        if (arrive(a.ws_gcnt + gslot) != kj - 1) return;
+        merge(a.ws_acc, a.ws_ml, base + (int64_t)j * f1, kj, m, l, ac);
+        store_record(a.ws_gacc + gslot * kMultiCols * D, a.ws_gml + gslot * kMultiCols * 2, kMultiCols * D * 4, c,
+                     m, l, ac, true);
+        reset(a.ws_gcnt + gslot);
+        if (arrive(a.ws_cnt + unit) != ng - 1) return;
+        merge(a.ws_gacc, a.ws_gml, base, ng, m, l, ac);
+        finalize(u, m, l, ac);
+        reset(a.ws_cnt + unit);
+    };
+
+    // ---- main loop over [g0, g1), one outer iteration per segment, kMDepth
+    // sub-tiles in flight (same structure as the single-query kernel)
+    u32x4 kbuf[kMDepth][NLK];
+    VReg vbuf[kMDepth][4];
+    MCursor cp = cur;
+    MCursor cl = cur;
+    int gl = g0;
+    issue(cl, true, kbuf[0], vbuf[0]);
+    static_for<1, kMDepth - 1>([&]<int m>() {
+        const bool more = gl + 1 < g1;
+        if (more) {
+            advance(cl);
+            ++gl;
+        }
+        issue(cl, more, kbuf[m], vbuf[m]);
+    });
+    int g = g0;
+    while (true) {
+        start_unit(cp);
+        seg_first = g;
+        int brk = 0;
+        bool done = false;
+        while (!done) {
+            static_for<0, kMDepth>([&]<int i>() {
+                if (done) return;
+                constexpr int nb = (i + kMDepth - 1) % kMDepth;
+                const bool more = gl + 1 < g1;
+                if (more) {
+                    advance(cl);
+                    ++gl;
+                }
+                issue(cl, more, kbuf[nb], vbuf[nb]);
+                process(cp, kbuf[i], vbuf[i]);
+                if (cp.sub + 1 == cp.n || g + 1 == g1) {
+                    brk = i;
+                    done = true;
+                    return;
+                }
+                advance(cp);
+                ++g;
+            });
+        }
+        finish_unit(cp, g);
+        if (g + 1 >= g1) break;
+        advance(cp);
+        ++g;
+        static_for<0, kMDepth - 1>([&]<int b>() {
+            if (brk == b) {
+                u32x4 tk[kMDepth][NLK];
+                VReg tv[kMDepth][4];
+                static_for<0, kMDepth>([&]<int m>() {
+                    static_for<0, NLK>([&]<int e>() { tk[m][e] = kbuf[m][e]; });
+                    static_for<0, 4>([&]<int e>() { tv[m][e] = vbuf[m][e]; });
+                });
+                static_for<0, kMDepth - 1>([&]<int m>() {
+                    constexpr int from = (b + 1 + m) % kMDepth;
+                    static_for<0, NLK>([&]<int e>() { kbuf[m][e] = tk[from][e]; });
+                    static_for<0, 4>([&]<int e>() { vbuf[m][e] = tv[from][e]; });
+                });
+            }
+        });
+    }
+}
+
+template <typename DT, int D>
+hipError_t launch_multi_typed(const MultiArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.num_waves / kWavesPerGroup));
+    attn_multi_kernel<DT, D><<<grid, dim3(kWavesPerGroup * kWave), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <typename DT, int D>
+int multi_waves_typed() {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_multi_kernel<DT, D>, kWavesPerGroup * kWave, 0) !=
+        hipSuccess)
+        return 0;
+    return blocks * kWavesPerGroup;
+}
+
+}  // namespace
+
+bool multi_supported(int32_t dtype, int32_t head_dim) {
+    return (dtype == 1 || dtype == 2) && (head_dim == 64 || head_dim == 128);
+}
+
+int multi_waves_per_cu(int32_t dtype, int32_t head_dim) {
+    static std::atomic<int> cache[2][2];
+    if (!multi_supported(dtype, head_dim)) return 0;
+    const int di = dtype - 1, hi = head_dim == 128 ? 1 : 0;
+    int v = cache[di][hi].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (dtype == 1) v = head_dim == 128 ? multi_waves_typed<F16, 128>() : multi_waves_typed<F16, 64>();
+    else v = head_dim == 128 ? multi_waves_typed<BF16, 128>() : multi_waves_typed<BF16, 64>();
+    if (v > 0) cache[di][hi].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+hipError_t launch_attn_multi(int32_t dtype, int32_t head_dim, const MultiArgs &a, hipStream_t stream) {
+    if (dtype == 1) {
+        return head_dim == 128 ? launch_multi_typed<F16, 128>(a, stream) : launch_multi_typed<F16, 64>(a, stream);
+    }
+    if (dtype == 2) {
+        return head_dim == 128 ? launch_multi_typed<BF16, 128>(a, stream) : launch_multi_typed<BF16, 64>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -191,9 +191,198 @@ int decode_impl(void *out, const void *q, const void *k_new, const void *v_new,
                : PKV_ERR_HIP;
 }
 
+// Units of the multi-query kernel for these sizes (an upper bound in the
+// shared-prefix case, where group sizes live on the device).
+int64_t multi_units(int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads) {
+    const int64_t cols = (int64_t)num_query_tokens * (num_q_heads / num_kv_heads);
+    return (int64_t)num_seqs * num_kv_heads * ((cols + pkv::kMultiCols - 1) / pkv::kMultiCols);
+}
+int64_t shared_units(int32_t num_seqs, int32_t num_groups, int32_t num_q_heads, int32_t num_kv_heads) {
+    const int64_t G = num_q_heads / num_kv_heads;
+    // prefix rows: sum over groups of ceil(members * G / 16) <= ceil(S * G / 16) + groups
+    const int64_t pre = (int64_t)num_kv_heads * (((int64_t)num_seqs * G + pkv::kMultiCols - 1) / pkv::kMultiCols +
+                                                 num_groups);
+    const int64_t suf = (int64_t)num_seqs * num_kv_heads;
+    return pre > suf ? pre : suf;
+}
+
+int log2_exact(int32_t x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return (1 << s) == x ? s : -1;
+}
+
+// Host checks shared by the multi-query entry points.
+int multi_checks(const void *out, const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                 int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len, float scale,
+                 int32_t dtype, int64_t units) {
+    if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
+        return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return PKV_ERR_SHAPE;
+    if (num_seqs > 65535 || num_kv_heads > 65535 || num_q_heads > 65535) return PKV_ERR_SHAPE;
+    if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+    if (!pkv::multi_supported(dtype, head_dim)) return PKV_ERR_UNSUPPORTED;
+    const int bsh = log2_exact(block_size);
+    if (bsh < 4 || bsh > 8) return PKV_ERR_UNSUPPORTED;   // 16 .. 256 tokens, a power of two
+    if (units > pkv::kMaxUnits) return PKV_ERR_UNSUPPORTED;
+    // sub-tile indices of the whole call are kept in 32 bits
+    if (units * (((int64_t)max_context_len + 15) / 16 + 1) >= ((int64_t)1 << 31)) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_ALIGN;
+    return PKV_OK;
+}
+
+int multi_waves(int32_t dtype, int32_t head_dim, int64_t *waves) {
+    int device = 0, cus = 0;
+    if (hipGetDevice(&device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return PKV_ERR_HIP;
+    int per_cu = pkv::multi_waves_per_cu(dtype, head_dim);
+    if (per_cu <= 0 || cus <= 0) return PKV_ERR_HIP;
+    per_cu = per_cu < 4 * pkv::kWavesPerSimd ? per_cu : 4 * pkv::kWavesPerSimd;
+    int64_t w = (int64_t)cus * per_cu;
+    w = w < pkv::kMaxWaves ? w : pkv::kMaxWaves;
+    w -= w % pkv::kWavesPerGroup;
+    *waves = w;
+    return PKV_OK;
+}
+
+void fill_multi_split(pkv::MultiArgs &a, const pkv::MultiWorkspace &ws, void *workspace) {
+    char *w = static_cast<char *>(workspace);
+    a.ws_cnt = reinterpret_cast<int32_t *>(w + ws.split.cnt_offset);
+    a.ws_gcnt = reinterpret_cast<int32_t *>(w + ws.split.gcnt_offset);
+    a.ws_acc = reinterpret_cast<float *>(w + ws.split.acc_offset);
+    a.ws_ml = reinterpret_cast<float *>(w + ws.split.ml_offset);
+    a.ws_gacc = reinterpret_cast<float *>(w + ws.split.gacc_offset);
+    a.ws_gml = reinterpret_cast<float *>(w + ws.split.gml_offset);
+    a.pre_acc = reinterpret_cast<float *>(w + ws.pre_acc_offset);
+    a.pre_ml = reinterpret_cast<float *>(w + ws.pre_ml_offset);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t paged_attn_decode_multi_workspace_size(int32_t num_seqs, int32_t num_query_tokens,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim) {
+    if (num_seqs <= 0 || num_query_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_q_heads % num_kv_heads != 0 || num_seqs > 65535 || num_query_tokens > 65535)
+        return 0;
+    const int64_t units = multi_units(num_seqs, num_query_tokens, num_q_heads, num_kv_heads);
+    if (units > pkv::kMaxUnits) return 0;
+    return pkv::multi_workspace(units, 0, head_dim).bytes;
+}
+
+int paged_attn_decode_multi(void *out, const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+                            int32_t num_query_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                            int64_t num_blocks, int32_t max_context_len, float scale, int32_t dtype,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_query_tokens <= 0 || num_query_tokens > 65535) return PKV_ERR_SHAPE;
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (num_seqs < 0) return PKV_ERR_SHAPE;
+    const int64_t units = multi_units(num_seqs, num_query_tokens, num_q_heads, num_kv_heads);
+    int st = multi_checks(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                          num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                          scale, dtype, units);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    const pkv::MultiWorkspace ws = pkv::multi_workspace(units, 0, head_dim);
+    if (!workspace || workspace_bytes < ws.bytes) return PKV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
+    int64_t waves = 0;
+    if ((st = multi_waves(dtype, head_dim, &waves)) != PKV_OK) return st;
+    pkv::MultiArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    fill_multi_split(a, ws, workspace);
+    a.mode = pkv::kModeMulti;
+    a.num_rows = num_seqs;
+    a.num_seqs = num_seqs;
+    a.max_units = (int32_t)units;
+    a.num_query_tokens = num_query_tokens;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_shift = log2_exact(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.num_waves = (int32_t)waves;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    return pkv::launch_attn_multi(dtype, head_dim, a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t paged_attn_decode_shared_workspace_size(int32_t num_seqs, int32_t num_groups, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim) {
+    if (num_seqs <= 0 || num_groups <= 0 || num_groups > num_seqs || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        head_dim <= 0 || num_q_heads % num_kv_heads != 0 || num_seqs > 65535)
+        return 0;
+    const int64_t units = shared_units(num_seqs, num_groups, num_q_heads, num_kv_heads);
+    if (units > pkv::kMaxUnits) return 0;
+    return pkv::multi_workspace(units, (int64_t)num_seqs * num_q_heads, head_dim).bytes;
+}
+
+int paged_attn_decode_shared(void *out, const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, const int32_t *context_lens,
+                             const int32_t *group_starts, const int32_t *prefix_lens, int32_t num_seqs,
+                             int32_t num_groups, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_context_len, float scale, int32_t dtype, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (num_seqs < 0 || num_groups < 0 || num_groups > num_seqs || (num_seqs > 0 && num_groups == 0))
+        return PKV_ERR_SHAPE;
+    const int64_t units = shared_units(num_seqs, num_groups, num_q_heads, num_kv_heads);
+    int st = multi_checks(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                          num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                          scale, dtype, units);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    if (!group_starts || !prefix_lens) return PKV_ERR_NULL;
+    const pkv::MultiWorkspace ws = pkv::multi_workspace(units, (int64_t)num_seqs * num_q_heads, head_dim);
+    if (!workspace || workspace_bytes < ws.bytes) return PKV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
+    int64_t waves = 0;
+    if ((st = multi_waves(dtype, head_dim, &waves)) != PKV_OK) return st;
+    pkv::MultiArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.group_starts = group_starts;
+    a.prefix_lens = prefix_lens;
+    fill_multi_split(a, ws, workspace);
+    a.num_query_tokens = 1;
+    a.num_seqs = num_seqs;
+    a.max_units = (int32_t)units;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_shift = log2_exact(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.num_waves = (int32_t)waves;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    // the shared prefix of every group once for all its members, then each
+    // sequence's own suffix merged with its prefix record (stream order)
+    a.mode = pkv::kModePrefix;
+    a.num_rows = num_groups;
+    if (pkv::launch_attn_multi(dtype, head_dim, a, stream) != hipSuccess) return PKV_ERR_HIP;
+    a.mode = pkv::kModeSuffix;
+    a.num_rows = num_seqs;
+    return pkv::launch_attn_multi(dtype, head_dim, a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
 
 int paged_attn_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, const int32_t *context_lens,

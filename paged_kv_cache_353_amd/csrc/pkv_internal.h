@@ -115,4 +115,69 @@ int decode_waves_per_cu(int32_t dtype, int32_t head_dim, int32_t group);
 hipError_t launch_attn_decode(int32_t dtype, int32_t head_dim, int32_t group,
                               const DecodeArgs &a, hipStream_t stream);
 
+// ------------------------------------------------ many query columns per KV head
+// One kernel serves three row kinds.  A row is a sequence or a group of
+// sequences; each of its (KV head, column chunk) units streams the row's
+// tokens once for up to kMultiCols query columns.
+enum MultiMode : int32_t {
+    kModeMulti = 0,   // rows = sequences; columns = (query token, head), causal among the new tokens
+    kModePrefix = 1,  // rows = groups; tokens [0, P) shared by every member; columns = (member, head);
+                      // writes one (max, exp-sum, acc) record per (sequence, q head)
+    kModeSuffix = 2,  // rows = sequences; tokens [P, L); columns = heads; folds in the record
+};
+constexpr int kMultiCols = 16;  // query columns per unit (the MFMA's N)
+
+struct MultiArgs {
+    void *out;
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    const int32_t *group_starts;  // shared modes: [num_groups + 1]
+    const int32_t *prefix_lens;   // shared modes: [num_seqs]
+    float *pre_acc;               // shared modes: [num_seqs * num_q_heads][head_dim]
+    float *pre_ml;                // shared modes: [num_seqs * num_q_heads][2]
+    int32_t *ws_cnt;
+    int32_t *ws_gcnt;
+    float *ws_acc;                // [kMaxWaves + units][kMultiCols][head_dim]
+    float *ws_ml;                 // [kMaxWaves + units][kMultiCols][2]
+    float *ws_gacc;
+    float *ws_gml;
+    int32_t mode;
+    int32_t num_rows;             // sequences, or groups in the prefix mode
+    int32_t num_seqs;
+    int32_t max_units;            // units the workspace holds
+    int32_t num_query_tokens;     // multi mode (1 otherwise)
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t block_shift;          // log2(block_size)
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;
+    int32_t num_waves;
+    float scale_log2;
+};
+
+struct MultiWorkspace {
+    DecodeWorkspace split;   // counters and partial records, sized for kMultiCols columns
+    size_t pre_acc_offset;   // prefix records (shared modes)
+    size_t pre_ml_offset;
+    size_t bytes;
+};
+
+inline MultiWorkspace multi_workspace(int64_t max_units, int64_t pre_records, int32_t head_dim) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    MultiWorkspace w{};
+    // decode_workspace sizes its slots for num_seqs * num_kv_heads units
+    w.split = decode_workspace((int32_t)max_units, 1, kMultiCols, head_dim);
+    w.pre_acc_offset = w.split.bytes;
+    w.pre_ml_offset = w.pre_acc_offset + up((size_t)pre_records * (size_t)head_dim * sizeof(float));
+    w.bytes = w.pre_ml_offset + up((size_t)pre_records * 2 * sizeof(float));
+    return w;
+}
+
+bool multi_supported(int32_t dtype, int32_t head_dim);
+int multi_waves_per_cu(int32_t dtype, int32_t head_dim);
+hipError_t launch_attn_multi(int32_t dtype, int32_t head_dim, const MultiArgs &a, hipStream_t stream);
+
 }  // namespace pkv

@@ -311,6 +311,28 @@ def shared_prefix(device="cpu", prompt_len: int = 1024, num_prompts: int = 16,
                   groups=[sample_ids[i:i + samples] for i in range(0, S, samples)]))
 
 
+def multi_query(inputs: DecodeInputs, num_query_tokens: int, seed: int) -> torch.Tensor:
+    """Queries for several new tokens per sequence: N(0,1) values of shape
+    [num_seqs, num_query_tokens, num_q_heads, head_dim] in the inputs' dtype.
+    The new tokens themselves are the last ``num_query_tokens`` positions of
+    each sequence, whose K/V the cache already holds."""
+    gen = torch.Generator(device=inputs.q.device)
+    gen.manual_seed(int(seed))
+    S, Hq, D = inputs.q.shape
+    q = torch.empty((S, int(num_query_tokens), Hq, D), dtype=inputs.q.dtype, device=inputs.q.device)
+    _randn_into(q, gen)
+    return q
+
+
+def speculative_llama8b(device="cpu", num_query_tokens: int = 4) -> tuple:
+    """The Llama-8B-shaped batch (64 sequences, lengths uniform in [128, 2048],
+    32 q / 8 kv heads, head_dim 128, bf16, block_size 16) verifying
+    ``num_query_tokens`` drafted tokens per sequence: returns (inputs, q)."""
+    inp = llama8b_decode(device)
+    inp.name = f"llama8b_bf16_bs16_q{num_query_tokens}"
+    return inp, multi_query(inp, num_query_tokens, seed_for(2) + 17)
+
+
 CONFIG_BUILDERS = {
     1: tiny,
     2: llama8b_decode,

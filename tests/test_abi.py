@@ -183,3 +183,48 @@ def test_copy_blocks_rejects_bad_arguments_on_host(lib):
     assert cp(bs=0) == PKV_ERR_SHAPE
     assert cp(k=(1 << 12) + 4) == PKV_ERR_ALIGN
     assert cp(Hkv=1, bs=1, D=2, dtype=1) == PKV_ERR_ALIGN   # 4-byte blocks
+
+
+def test_multi_and_shared_reject_bad_arguments_on_host(lib):
+    def multi(**kw):
+        a = dict(out=1 << 12, q=1 << 12, k=1 << 12, v=1 << 12, bt=1 << 12, cl=1 << 12, S=4, T=3, Hq=32,
+                 Hkv=8, D=128, bs=16, mb=16, nb=64, maxL=256, scale=0.1, dtype=2, ws=None, wsb=0)
+        a.update(kw)
+        return lib.paged_attn_decode_multi(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["T"],
+                                           a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"], a["maxL"],
+                                           a["scale"], a["dtype"], a["ws"], a["wsb"], None)
+
+    def shared(**kw):
+        a = dict(out=1 << 12, q=1 << 12, k=1 << 12, v=1 << 12, bt=1 << 12, cl=1 << 12, gs=1 << 12, pl=1 << 12,
+                 S=4, NG=2, Hq=32, Hkv=8, D=128, bs=16, mb=16, nb=64, maxL=256, scale=0.1, dtype=2, ws=None,
+                 wsb=0)
+        a.update(kw)
+        return lib.paged_attn_decode_shared(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["gs"], a["pl"],
+                                            a["S"], a["NG"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"],
+                                            a["maxL"], a["scale"], a["dtype"], a["ws"], a["wsb"], None)
+
+    for f in (multi, shared):
+        assert f(dtype=0) == PKV_ERR_UNSUPPORTED          # fp32 caches: single-query kernels only
+        assert f(dtype=7) == PKV_ERR_DTYPE
+        assert f(D=96) == PKV_ERR_UNSUPPORTED
+        assert f(bs=48, mb=8) == PKV_ERR_UNSUPPORTED      # not a power of two
+        assert f(bs=8, mb=32) == PKV_ERR_UNSUPPORTED
+        assert f(Hq=30) == PKV_ERR_SHAPE
+        assert f(mb=8) == PKV_ERR_SHAPE                   # table too short for max_context_len
+        assert f(out=None) == PKV_ERR_NULL
+        assert f(q=(1 << 12) + 8) == PKV_ERR_ALIGN
+        assert f() == PKV_ERR_WORKSPACE
+    assert multi(S=0) == PKV_OK
+    assert shared(S=0, NG=0) == PKV_OK
+    assert multi(Hq=24, Hkv=8) == PKV_ERR_WORKSPACE      # any group size is accepted
+    assert multi(T=0) == PKV_ERR_SHAPE
+    assert shared(gs=None) == PKV_ERR_NULL
+    assert shared(NG=0) == PKV_ERR_SHAPE
+    assert shared(NG=5) == PKV_ERR_SHAPE                 # more groups than sequences
+    ws = pkv.paged_attn_decode_multi_workspace_size(4, 3, 32, 8, 128)
+    assert ws > COUNTER_BYTES and ws % 256 == 0
+    assert pkv.paged_attn_decode_multi_workspace_size(4, 3, 32, 8, 128) < \
+        pkv.paged_attn_decode_multi_workspace_size(4, 9, 32, 8, 128)     # more column chunks
+    assert pkv.paged_attn_decode_shared_workspace_size(4, 2, 32, 8, 128) > 0
+    assert pkv.paged_attn_decode_shared_workspace_size(4, 5, 32, 8, 128) == 0
+    assert multi(ws=(1 << 12) + 16, wsb=ws) == PKV_ERR_ALIGN
