@@ -162,6 +162,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--query-tokens", type=int, default=4,
+                    help="also time several query tokens per sequence (Llama-8B batch; 0 = skip)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -250,6 +252,43 @@ def main() -> int:
     torch.cuda.synchronize()
     warm_us = warm[0].elapsed_time(warm[1]) / 20 * 1e3
 
+    extras = {}
+    if args.workload == "shared_prefix":
+        # the same decode with each group's shared prefix streamed once for
+        # all its forks (group description derived on the host, untimed)
+        from paged_kv_cache_353_amd.sharing import shared_prefix_groups
+        gs, pl = shared_prefix_groups(base.block_tables.cpu().numpy(), base.lens, base.block_size)
+        gs_d = torch.from_numpy(gs).to(dev)
+        pl_d = torch.from_numpy(pl).to(dev)
+        sws = torch.zeros(max(1, pkv.paged_attn_decode_shared_workspace_size(S, len(gs) - 1, Hq, Hkv, D)),
+                          dtype=torch.uint8, device=dev)
+        shared_us = timed(lambda s, o: pkv.paged_attn_decode_shared(
+            o, s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens, gs_d, pl_d, s.block_size, s.scale,
+            max_context_len=maxL, workspace=sws), K)
+        extras["shared_prefix_decode"] = {
+            "entry_point": "paged_attn_decode_shared (prefix once per group, then suffixes; two launches)",
+            "groups": len(gs) - 1, "shared_tokens_per_group": int(pl[0]),
+            "us": round(shared_us, 3),
+            "unique_kv_gbs": round(kv_unique / (shared_us * 1e-6) / 1e9, 2),
+            "logical_kv_gbs": round(kv_bytes / (shared_us * 1e-6) / 1e9, 2),
+            "speedup_vs_decode_only": round(decode_only_us / shared_us, 3)}
+    if args.workload == "llama8b" and args.query_tokens > 0:
+        # several query tokens per sequence (draft verification) on the same batch
+        from paged_kv_cache_353_amd.workloads import multi_query
+        T = args.query_tokens
+        q4s = [multi_query(x, T, 353_019) for x in sets]
+        o4s = [torch.empty_like(x) for x in q4s]
+        mws = torch.zeros(max(1, pkv.paged_attn_decode_multi_workspace_size(S, T, Hq, Hkv, D)),
+                          dtype=torch.uint8, device=dev)
+        idx = {id(x): k for k, x in enumerate(sets)}
+        multi_us = timed(lambda s, o: pkv.paged_attn_decode_multi(
+            o4s[idx[id(s)]], q4s[idx[id(s)]], s.k_cache, s.v_cache, s.block_tables, s.context_lens,
+            s.block_size, s.scale, max_context_len=maxL, workspace=mws), K)
+        extras["multi_query_decode"] = {
+            "entry_point": f"paged_attn_decode_multi ({T} query tokens per sequence, causal)",
+            "us": round(multi_us, 3), "kv_gbs": round(kv_bytes / (multi_us * 1e-6) / 1e9, 2),
+            "query_tokens_per_s": round(S * T / (multi_us * 1e-6), 1)}
+
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (launch_us * 1e-6) / 1e9
     traffic = traffic_for(base.name)
@@ -283,6 +322,7 @@ def main() -> int:
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "parity_worst_normwise": worst,
+        **extras,
         "kernel_source": source_digest(),
     }
     if not args.no_cpu_baseline:

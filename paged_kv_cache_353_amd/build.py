@@ -20,6 +20,11 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 
 SOURCES = ["kv_write.hip", "attn_decode.hip", "attn_multi.hip", "pkv_api.cpp"]
+# Per-source extra flags.  The many-column kernel accumulates its output with
+# MFMA and also scales it on the VALU; left to itself the compiler keeps the
+# accumulators in AGPRs and copies them to and from VGPRs around every
+# sub-tile.  The VGPR form of the MFMA instructions keeps them in one place.
+EXTRA_FLAGS = {"attn_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 
@@ -40,7 +45,7 @@ def compile_flags() -> list:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + compile_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + compile_flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

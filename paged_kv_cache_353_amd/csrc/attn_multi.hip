@@ -20,8 +20,9 @@
 //    from V rows 4r..4r+3 that lane (r, c) loaded, dims c*DL..c*DL+DL-1, by
 //    pairing the same element of the four rows.  Lane (r, j) ends up owning
 //    dims [r*D/4, (r+1)*D/4) of column j.
-// Softmax keeps one running (max, exp-sum) per column; a tile's column max
-// takes two lane exchanges across the row groups.
+// Softmax keeps one running (reference, exp-sum) per column.  The reference is
+// raised lazily, only when a score exceeds it by more than 8 in base-2 units,
+// so most sub-tiles need no exchange between the lanes of a column.
 //
 // Work split, masking and merging follow the single-query kernel: every
 // (row, KV head, column chunk) unit is cut into 16-token sub-tiles, all
@@ -44,6 +45,10 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMDirectMerge = 8;  // units split in at most this many pieces merge in one level
 constexpr int kMDepth = 2;        // sub-tiles in flight per wave
+constexpr int kMinTilesPerWave = 1;  // fewer waves than resident when the call is small
+constexpr float kLazyRescale = 8.f;  // headroom of the softmax reference (weights < 2^8)
+constexpr int kWeightOld = 3;     // relative share of the first half of the grid ...
+constexpr int kWeightYoung = 2;   // ... and of the second half
 
 // Position of a wave's load or compute stage.  Every field is wave-uniform.
 struct MCursor {
@@ -203,11 +208,27 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     // a group description that breaks its preconditions (overlapping groups)
     // could ask for more units than the workspace holds: do nothing then
     if (uniform(wave_sum_i(U, lane)) > a.max_units) return;
-    const int Weff = T < W ? T : W;
+    int Weff = T / kMinTilesPerWave;
+    Weff = Weff < 1 ? 1 : (Weff < W ? Weff : W);
     if (wave >= Weff) return;
-    auto start_of = [&](int w) -> int { return (int)((int64_t)T * w / Weff); };
+    // Range boundaries.  The first half of a full grid is dispatched first,
+    // so each of its waves is the older of the two on its SIMD, and the issue
+    // arbiter favours it: it streams about 1.5 times as fast.  Its ranges are
+    // made longer by kWeightOld : kWeightYoung so that both halves end
+    // together.  The split depends only on T and W, so results stay
+    // deterministic.
+    const bool weighted = kWeightOld != kWeightYoung && Weff == W && T >= 4 * W;
+    const int wa = weighted ? kWeightOld : 1;
+    const int wb = weighted ? kWeightYoung : 1;
+    const int half = Weff / 2;
+    auto cum = [&](int w) -> int64_t {
+        return (int64_t)wa * min(w, half) + (int64_t)wb * max(w - half, 0);
+    };
+    const int64_t cum_all = cum(Weff);
+    auto start_of = [&](int w) -> int { return (int)((int64_t)T * cum(w) / cum_all); };
     auto wave_of = [&](int x) -> int {  // the largest w with start_of(w) <= x
-        int w = (int)(((int64_t)x * Weff) / T);
+        const int64_t t = (int64_t)x * cum_all / T;
+        int w = t <= (int64_t)wa * half ? (int)(t / wa) : half + (int)((t - (int64_t)wa * half) / wb);
         w = min(max(w, 0), Weff - 1);
         while (w + 1 < Weff && start_of(w + 1) <= x) ++w;
         while (w > 0 && start_of(w) > x) --w;
@@ -363,18 +384,25 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             sv[r] = (t >= lo && t < lim) ? s[r] * a.scale_log2 : kNegInf;
             tmax = fmaxf(tmax, sv[r]);
         });
-        tmax = fmaxf(tmax, xor16(tmax));
-        tmax = fmaxf(tmax, xor32(tmax, lane));
-        const float m_new = fmaxf(m_run, tmax);
-        const float mu = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - mu);
+        // The exponentials are taken against the column's reference m_run,
+        // which is raised (and the state rescaled) only when some score of
+        // the wave exceeds its column's reference by more than kLazyRescale
+        // (base-2 units).  Weights therefore stay below 2^kLazyRescale, and
+        // the common sub-tile needs no exchange between the row groups.  The
+        // first valid score of a column always raises its reference.
+        if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazyRescale) != 0) {
+            float cm = fmaxf(tmax, xor16(tmax));
+            cm = fmaxf(cm, xor32(cm, lane));
+            const float m_new = fmaxf(m_run, cm);
+            const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+            l_run *= alpha;
+            static_for<0, DL>([&]<int e>() { acc[e] *= alpha; });
+            m_run = m_new;
+        }
+        const float mu = m_run == kNegInf ? 0.f : m_run;
         float p[4];
         static_for<0, 4>([&]<int r>() { p[r] = fast_exp2(sv[r] - mu); });
-        l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-            static_for<0, DL>([&]<int e>() { acc[e] *= alpha; });
-        }
+        l_run += (p[0] + p[1]) + (p[2] + p[3]);
         if constexpr (std::is_same_v<DT, BF16>) {
             u32x2 ph, pl;
             split_probs_bf16(p, ph, pl);
@@ -413,9 +441,11 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         });
     };
     // Stores a (max, exp-sum, acc) record of this lane's column: acc at
-    // racc + col * D, (max, sum) at rml + 2 * col.
+    // racc + col * D, (max, sum) at rml + 2 * col.  Lanes of absent columns
+    // store nothing.
     auto store_record = [&](float *racc, float *rml, int racc_bytes, int col, float m, float l,
                             const f32x4 (&ac)[DL], bool coherent) {
+        if (orow < 0) return;
         static_for<0, 4>([&]<int i>() {
             static_for<0, DL / 4>([&]<int v>() {
                 const f32x4 x = {ac[4 * v][i], ac[4 * v + 1][i], ac[4 * v + 2][i], ac[4 * v + 3][i]};
@@ -445,29 +475,55 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         });
         m = mn;
     };
-    // Loads this lane's part of record `slot` (acc in [i * DL + e] order).
-    auto load_record = [&](const float *racc, const float *rml, int64_t slot, float &m, float &l,
-                           f32x4 (&ac)[DL]) {
-        const float *ra = racc + slot * kMultiCols * D;
-        const float *rm = rml + slot * kMultiCols * 2;
-        static_for<0, 4>([&]<int i>() {
-            static_for<0, DL / 4>([&]<int v>() {
-                const f32x4 x = load_coherent(ra, kMultiCols * D * 4, (c * D + rg * DQ + i * DL + 4 * v) * 4);
-                static_for<0, 4>([&]<int k>() { ac[4 * v + k][i] = x[k]; });
-            });
-        });
-        m = __hip_atomic_load(rm + 2 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        l = __hip_atomic_load(rm + 2 * c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    // Merges records [first, first + cnt) in index order.
+    // Merges records [first, first + cnt) into (m, l, ac), in index order.
+    // Per block of kMergeBlock records: their (max, sum) pairs in one round
+    // trip, then their acc rows one record after another.
+    // Absent columns load nothing (out-of-range offsets read as zero).
+    constexpr int kMergeBlock = 8;
     auto merge = [&](const float *racc, const float *rml, int64_t first, int cnt, float &m, float &l,
                      f32x4 (&ac)[DL]) {
-        load_record(racc, rml, first, m, l, ac);
-        for (int r = 1; r < cnt; ++r) {
-            float m2, l2;
-            f32x4 a2[DL];
-            load_record(racc, rml, first + r, m2, l2, a2);
-            fold(m, l, ac, m2, l2, a2);
+        m = kNegInf;
+        l = 0.f;
+        static_for<0, DL>([&]<int e>() { ac[e] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+        const int aoff = orow >= 0 ? (c * D + rg * DQ) * 4 : 0x7FFFF000;
+        for (int r0 = 0; r0 < cnt; r0 += kMergeBlock) {
+            float mb[kMergeBlock], lb[kMergeBlock];
+            static_for<0, kMergeBlock>([&]<int b>() {
+                const int64_t rr = first + (r0 + b < cnt ? r0 + b : 0);
+                const float *rm = rml + rr * kMultiCols * 2 + 2 * c;
+                mb[b] = __hip_atomic_load(rm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                lb[b] = __hip_atomic_load(rm + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (r0 + b >= cnt) {
+                    mb[b] = kNegInf;
+                    lb[b] = 0.f;
+                }
+            });
+            float mn = m;
+            static_for<0, kMergeBlock>([&]<int b>() { mn = fmaxf(mn, mb[b]); });
+            const float mu = mn == kNegInf ? 0.f : mn;
+            const float x = fast_exp2(m - mu);
+            l *= x;
+            static_for<0, DL>([&]<int e>() { ac[e] *= x; });
+            float w[kMergeBlock];
+            static_for<0, kMergeBlock>([&]<int b>() {
+                w[b] = fast_exp2(mb[b] - mu);
+                l = __builtin_fmaf(w[b], lb[b], l);
+            });
+            m = mn;
+            static_for<0, kMergeBlock>([&]<int b>() {
+                if (r0 + b < cnt) {
+                    const float *ra = racc + (first + r0 + b) * kMultiCols * D;
+                    f32x4 xa[DL];
+                    static_for<0, DL>([&]<int q>() { xa[q] = load_coherent(ra, kMultiCols * D * 4, aoff + q * 16); });
+                    // acc element (i, e) sits at float i * DL + e of the lane's slice
+                    static_for<0, DL>([&]<int q>() {
+                        static_for<0, 4>([&]<int k>() {
+                            constexpr int fl = 4 * q + k, i = fl / DL, e = fl % DL;
+                            ac[e][i] = __builtin_fmaf(w[b], xa[q][k], ac[e][i]);
+                        });
+                    });
+                }
+            });
         }
     };
     // The unit's result: output (multi), output merged with the prefix
@@ -502,47 +558,59 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
 
+    // Leaves the unit at `u` after sub-tile `g_last`.  A unit split between
+    // k waves is merged by the last to arrive: directly for k <= 8, else in
+    // two levels (groups of about sqrt(k) consecutive records first).  The
+    // merge and the final write each have one call site, which keeps the
+    // register footprint of the kernel down.
     auto finish_unit = [&](const MCursor &u, int g_last) {
         float l = column_sum(l_run);
         float m = m_run;
         const int ua = unit_first(u);
         const int ub = ua + u.n;
-        if (seg_first == ua && g_last + 1 == ub) {
-            finalize(u, m, l, acc);
-            return;
-        }
-        const int w_first = wave_of(ua);
-        const int w_last = wave_of(ub - 1);
-        const int k = w_last - w_first + 1;
-        const int unit = unit_index(u);
-        const int64_t base = (int64_t)w_first + unit;
-        const int64_t slot = (int64_t)wave + unit;
-        store_record(a.ws_acc + slot * kMultiCols * D, a.ws_ml + slot * kMultiCols * 2, kMultiCols * D * 4, c,
-                     m, l, acc, true);
-        f32x4 ac[DL];
-        if (k <= kMDirectMerge) {
-            if (arrive(a.ws_cnt + unit) != k - 1) return;
-            merge(a.ws_acc, a.ws_ml, base, k, m, l, ac);
-            finalize(u, m, l, ac);
+        if (!(seg_first == ua && g_last + 1 == ub)) {
+            const int w_first = wave_of(ua);
+            const int w_last = wave_of(ub - 1);
+            const int k = w_last - w_first + 1;
+            const int unit = unit_index(u);
+            const int64_t base = (int64_t)w_first + unit;
+            const int64_t slot = (int64_t)wave + unit;
+            store_record(a.ws_acc + slot * kMultiCols * D, a.ws_ml + slot * kMultiCols * 2, kMultiCols * D * 4,
+                         c, m, l, acc, true);
+            const float *racc = a.ws_acc;
+            const float *rml = a.ws_ml;
+            int64_t first = base;
+            int cnt = k;
+            int ng = 0;              // groups of the second level (0: one level)
+            int64_t gslot = 0;
+            if (k <= kMDirectMerge) {
+                if (arrive(a.ws_cnt + unit) != k - 1) return;
+            } else {
+                int f1 = (int)__builtin_sqrtf((float)k);
+                while (f1 * f1 < k) ++f1;
+                ng = (k + f1 - 1) / f1;
+                const int j = (wave - w_first) / f1;
+                cnt = min(f1, k - j * f1);
+                first = base + (int64_t)j * f1;
+                gslot = base + j;
+                if (arrive(a.ws_gcnt + gslot) != cnt - 1) return;
+            }
+            while (true) {
+                merge(racc, rml, first, cnt, m, l, acc);
+                if (ng == 0) break;
+                store_record(a.ws_gacc + gslot * kMultiCols * D, a.ws_gml + gslot * kMultiCols * 2,
+                             kMultiCols * D * 4, c, m, l, acc, true);
+                reset(a.ws_gcnt + gslot);
+                if (arrive(a.ws_cnt + unit) != ng - 1) return;
+                racc = a.ws_gacc;
+                rml = a.ws_gml;
+                first = base;
+                cnt = ng;
+                ng = 0;
+            }
             reset(a.ws_cnt + unit);
-            return;
         }
-        int f1 = (int)__builtin_sqrtf((float)k);
-        while (f1 * f1 < k) ++f1;
-        const int ng = (k + f1 - 1) / f1;
-        const int r = wave - w_first;
-        const int j = r / f1;
-        const int kj = min(f1, k - j * f1);
-        const int64_t gslot = base + j;
-        if (arrive(a.ws_gcnt + gslot) != kj - 1) return;
-        merge(a.ws_acc, a.ws_ml, base + (int64_t)j * f1, kj, m, l, ac);
-        store_record(a.ws_gacc + gslot * kMultiCols * D, a.ws_gml + gslot * kMultiCols * 2, kMultiCols * D * 4, c,
-                     m, l, ac, true);
-        reset(a.ws_gcnt + gslot);
-        if (arrive(a.ws_cnt + unit) != ng - 1) return;
-        merge(a.ws_gacc, a.ws_gml, base, ng, m, l, ac);
-        finalize(u, m, l, ac);
-        reset(a.ws_cnt + unit);
+        finalize(u, m, l, acc);
     };
 
     // ---- main loop over [g0, g1), one outer iteration per segment, kMDepth
@@ -591,21 +659,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         if (g + 1 >= g1) break;
         advance(cp);
         ++g;
-        static_for<0, kMDepth - 1>([&]<int b>() {
-            if (brk == b) {
-                u32x4 tk[kMDepth][NLK];
-                VReg tv[kMDepth][4];
-                static_for<0, kMDepth>([&]<int m>() {
-                    static_for<0, NLK>([&]<int e>() { tk[m][e] = kbuf[m][e]; });
-                    static_for<0, 4>([&]<int e>() { tv[m][e] = vbuf[m][e]; });
-                });
-                static_for<0, kMDepth - 1>([&]<int m>() {
-                    constexpr int from = (b + 1 + m) % kMDepth;
-                    static_for<0, NLK>([&]<int e>() { kbuf[m][e] = tk[from][e]; });
-                    static_for<0, 4>([&]<int e>() { vbuf[m][e] = tv[from][e]; });
-                });
-            }
-        });
+        // the next sub-tile sits in buffer (brk + 1) % 2: bring it to buffer 0
+        static_assert(kMDepth == 2, "buffer rotation written for two buffers");
+        if (brk == 0) {
+            static_for<0, NLK>([&]<int e>() { kbuf[0][e] = kbuf[1][e]; });
+            static_for<0, 4>([&]<int e>() { vbuf[0][e] = vbuf[1][e]; });
+        }
     }
 }
 

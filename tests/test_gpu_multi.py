@@ -109,3 +109,13 @@ def test_multi_with_one_token_matches_single_query_decode():
     # both within the oracle's tolerance of each other (different rounding of p)
     diff = (out1.float() - ref.float()).abs()
     assert float(diff.max()) <= 2e-3 + 1e-2 * float(ref.float().abs().max())
+
+
+@pytest.mark.parametrize("gain", [8.0, 40.0])
+def test_multi_wide_score_range(gain):
+    """Scores spread over many powers of two: the softmax reference is raised
+    many times inside a unit, and single tokens dominate some outputs."""
+    say(f"case: multi, queries scaled by {gain}")
+    inp = W.build_decode_inputs([5, 64, 700, 3000], 32, 8, 128, 16, "bf16", 300, seed=83, device=DEV)
+    q4 = (W.multi_query(inp, 3, seed=84).float() * gain).to(torch.bfloat16)
+    check_multi(inp, q4, what=f"multi gain {gain}")
