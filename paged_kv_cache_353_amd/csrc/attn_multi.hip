@@ -24,11 +24,11 @@
 // raised lazily, only when a score exceeds it by more than 8 in base-2 units,
 // so most sub-tiles need no exchange between the lanes of a column.
 //
-// Work split, masking and merging follow the single-query kernel: every
-// (row, KV head, column chunk) unit is cut into 16-token sub-tiles, all
-// sub-tiles are shared out in equal contiguous ranges, one per resident
-// wave; a unit split between k waves leaves k partial records that the last
-// arriver merges in a fixed order (two levels for large k).  Loads use
+// Work split and masking follow the single-query kernel: every (row, KV head,
+// column chunk) unit is cut into 16-token sub-tiles, and all sub-tiles are
+// shared out in equal contiguous ranges, one per resident wave.  A unit split
+// between k waves leaves k partial records; a second, short launch merges
+// them, every record of a unit in flight at once, in a fixed order.  Loads use
 // descriptors that span only the unit's valid rows, so rows past the end read
 // as zero, and every score outside a column's window is set to -inf before the
 // exponential, so stale cache contents never reach the result.
@@ -43,12 +43,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMDirectMerge = 8;  // units split in at most this many pieces merge in one level
 constexpr int kMDepth = 2;        // sub-tiles in flight per wave
-constexpr int kMinTilesPerWave = 1;  // fewer waves than resident when the call is small
+constexpr int kDescWords = 8;     // unit descriptor: first slot, records, row, kvh|chunk, tseq, cols, lo, -
 constexpr float kLazyRescale = 8.f;  // headroom of the softmax reference (weights < 2^8)
-constexpr int kWeightOld = 3;     // relative share of the first half of the grid ...
-constexpr int kWeightYoung = 2;   // ... and of the second half
 
 // Position of a wave's load or compute stage.  Every field is wave-uniform.
 struct MCursor {
@@ -117,7 +114,56 @@ __device__ __forceinline__ uint32_t v_half(const VR &v) {
     return (E & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-template <typename DT, int D>
+// A row of the many-column kernel: the token range it streams, the first
+// position its columns attend, its length, the sequence whose table it walks
+// and its query columns per KV head.  `ld` reads a 32-bit entry of a length
+// array (scalar or vector loads).
+struct RowInfo { int t0, tend, lo, L, tseq, cols; };
+
+template <typename LD>
+__device__ __forceinline__ RowInfo row_info_of(const MultiArgs &a, int r, LD ld) {
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int Lmax = a.max_context_len;
+    auto clampL = [&](int L) { L = L < Lmax ? L : Lmax; return L > 0 ? L : 0; };
+    RowInfo ri{};
+    if (a.mode == kModePrefix) {
+        // members clamped to the batch (the description is device data)
+        int f = ld(a.group_starts, r), e = ld(a.group_starts, r + 1);
+        f = min(max(f, 0), a.num_seqs);
+        e = min(max(e, f), a.num_seqs);
+        const int P = clampL(ld(a.prefix_lens, f));
+        ri.t0 = 0; ri.tend = P; ri.lo = 0; ri.L = P; ri.tseq = f; ri.cols = (e - f) * G;
+    } else if (a.mode == kModeSuffix) {
+        const int L = clampL(ld(a.context_lens, r));
+        int P = clampL(ld(a.prefix_lens, r));
+        P = P < L ? P : L;
+        // an empty suffix streams nothing (its output is the prefix record)
+        ri.t0 = P < L ? (P & ~15) : P; ri.tend = L; ri.lo = P; ri.L = L; ri.tseq = r; ri.cols = G;
+    } else {
+        const int L = clampL(ld(a.context_lens, r));
+        ri.t0 = 0; ri.tend = L; ri.lo = 0; ri.L = L; ri.tseq = r; ri.cols = a.num_query_tokens * G;
+    }
+    return ri;
+}
+
+// Output row of column x (0-based within its row) of KV head kvh, or -1 if
+// the row has no such column: an index into out ([.., Hq, D] rows) in the
+// multi and suffix modes, into the prefix records in the prefix mode.
+__device__ __forceinline__ int64_t column_row(const MultiArgs &a, int row, const RowInfo &ri, int kvh, int x) {
+    if (x >= ri.cols) return -1;
+    const int Hq = a.num_q_heads, G = Hq / a.num_kv_heads;
+    if (a.mode == kModeMulti) {
+        const int jq = x / G, h = x - jq * G;
+        return ((int64_t)row * a.num_query_tokens + jq) * Hq + kvh * G + h;
+    }
+    if (a.mode == kModePrefix) {
+        const int mem = x / G, h = x - mem * G;
+        return (int64_t)(ri.tseq + mem) * Hq + kvh * G + h;
+    }
+    return (int64_t)row * Hq + kvh * G + x;
+}
+
+template <typename DT, int D, int CH>
 __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(MultiArgs a) {
     constexpr int EB = DT::kBytes;
     static_assert(EB == 2, "16-bit caches only");
@@ -125,48 +171,27 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     constexpr int NLK = D / 32;      // 16-byte K loads per lane per sub-tile (one per 32-dim MFMA step)
     constexpr int DL = D / 16;       // dims of a V row per lane (and 16x16x16 MFMAs per sub-tile)
     constexpr int DQ = D / 4;        // output dims owned by a lane
+    constexpr int UC = kMultiCols * CH;   // query columns of a unit
+    constexpr int kRecFloats = UC * D;    // floats of a record's acc
     typedef typename std::conditional<DL == 8, u32x4, u32x2>::type VReg;
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    static_assert(CH >= 1 && CH <= kMultiChunksMax, "column chunks per unit");
 
     const int lane = threadIdx.x & (kWave - 1);
     const int rg = lane >> 4;   // row group: tokens 4rg..4rg+3 of a sub-tile
-    const int c = lane & 15;    // column (scores, output) / token row (K) / dim slice (V)
+    const int c = lane & 15;    // column within a chunk (scores, output) / token row (K) / dim slice (V)
     const int wave = uniform((int)blockIdx.x * kWavesPerGroup + (int)(threadIdx.x >> 6));
     const int R = a.num_rows, Hkv = a.num_kv_heads, Hq = a.num_q_heads;
     const int G = Hq / Hkv;
     const int Tq = a.num_query_tokens;
-    const int Lmax = a.max_context_len;
     const int W = a.num_waves;
     const int mode = a.mode;
-    auto clampL = [&](int L) { L = L < Lmax ? L : Lmax; return L > 0 ? L : 0; };
 
-    // ---- row description; `ld` reads a 32-bit entry of a length array
-    struct RowInfo { int t0, tend, lo, L, tseq, cols; };
-    auto row_info = [&](int r, auto ld) -> RowInfo {
-        RowInfo ri{};
-        if (mode == kModePrefix) {
-            // members clamped to the batch (the description is device data)
-            int f = ld(a.group_starts, r), e = ld(a.group_starts, r + 1);
-            f = min(max(f, 0), a.num_seqs);
-            e = min(max(e, f), a.num_seqs);
-            const int P = clampL(ld(a.prefix_lens, f));
-            ri.t0 = 0; ri.tend = P; ri.lo = 0; ri.L = P; ri.tseq = f; ri.cols = (e - f) * G;
-        } else if (mode == kModeSuffix) {
-            const int L = clampL(ld(a.context_lens, r));
-            int P = clampL(ld(a.prefix_lens, r));
-            P = P < L ? P : L;
-            // an empty suffix streams nothing (its output is the prefix record)
-            ri.t0 = P < L ? (P & ~15) : P; ri.tend = L; ri.lo = P; ri.L = L; ri.tseq = r; ri.cols = G;
-        } else {
-            const int L = clampL(ld(a.context_lens, r));
-            ri.t0 = 0; ri.tend = L; ri.lo = 0; ri.L = L; ri.tseq = r; ri.cols = Tq * G;
-        }
-        return ri;
-    };
+    auto row_info = [&](int r, auto ld) -> RowInfo { return row_info_of(a, r, ld); };
     auto ld_vec = [](const int32_t *p, int i) { return p[i]; };
     auto ld_scalar = [](const int32_t *p, int i) { return ((const_i32_ptr)p)[i]; };
     auto tiles_of = [&](const RowInfo &ri) { return (ri.tend - ri.t0 + 15) >> 4; };
-    auto chunks_of = [&](const RowInfo &ri) { return (ri.cols + kMultiCols - 1) / kMultiCols; };
+    auto chunks_of = [&](const RowInfo &ri) { return (ri.cols + UC - 1) / UC; };
 
     // ---- rows with nothing to stream: zero outputs, or (suffix mode) the
     // prefix record on its own
@@ -193,7 +218,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         }
     }
 
-    // ---- total work and this wave's range
+    // ---- total work and this wave's range (equal contiguous shares)
     int N = 0, U = 0;
     for (int base = 0; base < R; base += kWave) {
         const int r = base + lane;
@@ -207,28 +232,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     const int T = uniform(wave_sum_i(N, lane));
     // a group description that breaks its preconditions (overlapping groups)
     // could ask for more units than the workspace holds: do nothing then
-    if (uniform(wave_sum_i(U, lane)) > a.max_units) return;
-    int Weff = T / kMinTilesPerWave;
-    Weff = Weff < 1 ? 1 : (Weff < W ? Weff : W);
+    const int units = uniform(wave_sum_i(U, lane));
+    const bool too_many = units > a.max_units;
+    if (wave == 0 && lane == 0) a.unit_desc[0] = too_many ? 0 : units;   // units the reduce pass visits
+    if (too_many) return;
+    const int Weff = T < W ? T : W;
     if (wave >= Weff) return;
-    // Range boundaries.  The first half of a full grid is dispatched first,
-    // so each of its waves is the older of the two on its SIMD, and the issue
-    // arbiter favours it: it streams about 1.5 times as fast.  Its ranges are
-    // made longer by kWeightOld : kWeightYoung so that both halves end
-    // together.  The split depends only on T and W, so results stay
-    // deterministic.
-    const bool weighted = kWeightOld != kWeightYoung && Weff == W && T >= 4 * W;
-    const int wa = weighted ? kWeightOld : 1;
-    const int wb = weighted ? kWeightYoung : 1;
-    const int half = Weff / 2;
-    auto cum = [&](int w) -> int64_t {
-        return (int64_t)wa * min(w, half) + (int64_t)wb * max(w - half, 0);
-    };
-    const int64_t cum_all = cum(Weff);
-    auto start_of = [&](int w) -> int { return (int)((int64_t)T * cum(w) / cum_all); };
+    auto start_of = [&](int w) -> int { return (int)((int64_t)T * w / Weff); };
     auto wave_of = [&](int x) -> int {  // the largest w with start_of(w) <= x
-        const int64_t t = (int64_t)x * cum_all / T;
-        int w = t <= (int64_t)wa * half ? (int)(t / wa) : half + (int)((t - (int64_t)wa * half) / wb);
+        int w = (int)(((int64_t)x * Weff) / T);
         w = min(max(w, 0), Weff - 1);
         while (w + 1 < Weff && start_of(w + 1) <= x) ++w;
         while (w > 0 && start_of(w) > x) --w;
@@ -242,7 +254,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         u.t0 = uniform(ri.t0); u.tend = uniform(ri.tend); u.lo = uniform(ri.lo); u.L = uniform(ri.L);
         u.tseq = uniform(ri.tseq); u.cols = uniform(ri.cols);
         u.n = uniform((u.tend - u.t0 + 15) >> 4);
-        u.chunks = uniform((u.cols + kMultiCols - 1) / kMultiCols);
+        u.chunks = uniform((u.cols + UC - 1) / UC);
     };
 
     // ---- locate g0: row (prefix scans of sub-tiles and units), then unit and sub-tile
@@ -327,99 +339,100 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- per-unit state
-    u32x4 qr[NLK];        // B operand of the scores: column c (zero when absent)
-    int lim = 0;          // this lane's column attends positions [lo, lim)
-    int64_t orow = -1;    // multi/suffix: output row of this lane's column; prefix: record index
-    float m_run = kNegInf, l_run = 0.f;   // lane (rg, c): column c; l_run is this lane's share
-    f32x4 acc[DL];        // acc[e][i]: column c, dim (4rg + i) * DL + e
+    // ---- per-unit state, one set per column chunk ch: lane (rg, c) holds
+    // column ch * 16 + c of the unit
+    u32x4 qr[CH][NLK];       // B operand of the scores (zero for absent columns)
+    int lim[CH];             // the column attends positions [lo, lim)
+    int64_t orow[CH];        // multi/suffix: output row of the column; prefix: record index; -1 absent
+    float m_run[CH], l_run[CH];   // reference and this lane's share of the exp-sum
+    f32x4 acc[CH][DL];       // acc[ch][e][i]: dim (4rg + i) * DL + e
     int seg_first = g0;
 
     auto start_unit = [&](const MCursor &u) {
-        const int x = u.chunk * kMultiCols + c;     // column index within the row
-        const bool valid = x < u.cols;
-        int qrel = 0;                               // q row relative to the row's first q row
         int64_t qbase = 0;                          // first q row of the row
         int qspan = 0;                              // q rows of the row
         if (mode == kModeMulti) {
-            const int jq = x / G, h = x - jq * G;
             qbase = (int64_t)u.row * Tq * Hq;
             qspan = Tq * Hq;
-            qrel = jq * Hq + u.kvh * G + h;
-            lim = valid ? u.L - Tq + jq + 1 : 0;
         } else if (mode == kModePrefix) {
-            const int mem = x / G, h = x - mem * G;
             qbase = (int64_t)u.tseq * Hq;
             qspan = (u.cols / G) * Hq;
-            qrel = mem * Hq + u.kvh * G + h;
-            lim = valid ? u.L : 0;
         } else {
             qbase = (int64_t)u.row * Hq;
             qspan = Hq;
-            qrel = u.kvh * G + x;
-            lim = valid ? u.L : 0;
         }
-        orow = valid ? qbase + qrel : -1;
+        const RowInfo ri{u.t0, u.tend, u.lo, u.L, u.tseq, u.cols};
         const char *qb = static_cast<const char *>(a.q) + uniform(qbase * ROW);
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, uniform(qspan * ROW), kBufferFlags);
-        const int qoff = valid ? qrel * ROW + 16 * rg : 0x7FFFFF00;   // out of range: zero
-        static_for<0, NLK>([&]<int b>() { qr[b] = load_chunk(rq, qoff + 64 * b); });
+        static_for<0, CH>([&]<int ch>() {
+            const int x = (u.chunk * CH + ch) * kMultiCols + c;   // column index within the row
+            orow[ch] = column_row(a, u.row, ri, u.kvh, x);
+            const bool valid = orow[ch] >= 0;
+            if (mode == kModeMulti) lim[ch] = valid ? u.L - Tq + x / G + 1 : 0;
+            else lim[ch] = valid ? u.L : 0;
+            // q rows are the output rows (the prefix records are indexed the same way)
+            const int qoff = valid ? (int)(orow[ch] - qbase) * ROW + 16 * rg : 0x7FFFFF00;   // out of range: zero
+            static_for<0, NLK>([&]<int b>() { qr[ch][b] = load_chunk(rq, qoff + 64 * b); });
+            m_run[ch] = kNegInf;
+            l_run[ch] = 0.f;
+            static_for<0, DL>([&]<int e>() { acc[ch][e] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+        });
+        // wait for q here, so that the sub-tile loop is entered with nothing
+        // but its own loads in flight and its waits stay exact
 #pragma unroll
-        for (int b = 0; b < NLK; ++b) asm volatile("" ::"v"(qr[b]));
-        m_run = kNegInf;
-        l_run = 0.f;
-        static_for<0, DL>([&]<int e>() { acc[e] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+        for (int ch = 0; ch < CH; ++ch) {
+#pragma unroll
+            for (int b = 0; b < NLK; ++b) asm volatile("" ::"v"(qr[ch][b]));
+        }
     };
 
-    // One sub-tile: scores, the column-wise online softmax, O^T += V^T P.
+    // One sub-tile: scores, the column-wise online softmax, O^T += V^T P, for
+    // every column chunk of the unit (the V operand is packed once).
     auto process = [&](const MCursor &u, const u32x4 (&kr)[NLK], const VReg (&vr)[4]) {
         const int tok = u.t0 + (u.sub << 4) + 4 * rg;
         const int lo = u.lo;
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        static_for<0, NLK>([&]<int b>() { s = mfma_chunk<DT>(kr[b], qr[b], s); });
-        float sv[4];
-        float tmax = kNegInf;
-        static_for<0, 4>([&]<int r>() {
-            const int t = tok + r;
-            sv[r] = (t >= lo && t < lim) ? s[r] * a.scale_log2 : kNegInf;
-            tmax = fmaxf(tmax, sv[r]);
+        u32x2 ph[CH], pl[CH];
+        static_for<0, CH>([&]<int ch>() {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            static_for<0, NLK>([&]<int b>() { s = mfma_chunk<DT>(kr[b], qr[ch][b], s); });
+            float sv[4];
+            float tmax = kNegInf;
+            static_for<0, 4>([&]<int r>() {
+                const int t = tok + r;
+                sv[r] = (t >= lo && t < lim[ch]) ? s[r] * a.scale_log2 : kNegInf;
+                tmax = fmaxf(tmax, sv[r]);
+            });
+            // The exponentials are taken against the column's reference
+            // m_run, which is raised (and the state rescaled) only when some
+            // score of the wave exceeds its column's reference by more than
+            // kLazyRescale (base-2 units).  Weights therefore stay below
+            // 2^kLazyRescale, and the common sub-tile needs no exchange
+            // between the row groups.  The first valid score of a column
+            // always raises its reference.
+            if (__builtin_amdgcn_ballot_w64(tmax > m_run[ch] + kLazyRescale) != 0) {
+                float cm = fmaxf(tmax, xor16(tmax));
+                cm = fmaxf(cm, xor32(cm, lane));
+                const float m_new = fmaxf(m_run[ch], cm);
+                const float alpha = fast_exp2(m_run[ch] - (m_new == kNegInf ? 0.f : m_new));
+                l_run[ch] *= alpha;
+                static_for<0, DL>([&]<int e>() { acc[ch][e] *= alpha; });
+                m_run[ch] = m_new;
+            }
+            const float mu = m_run[ch] == kNegInf ? 0.f : m_run[ch];
+            float p[4];
+            static_for<0, 4>([&]<int r>() { p[r] = fast_exp2(sv[r] - mu); });
+            l_run[ch] += (p[0] + p[1]) + (p[2] + p[3]);
+            if constexpr (std::is_same_v<DT, BF16>) split_probs_bf16(p, ph[ch], pl[ch]);
+            else ph[ch] = pack_probs_f16(p);
         });
-        // The exponentials are taken against the column's reference m_run,
-        // which is raised (and the state rescaled) only when some score of
-        // the wave exceeds its column's reference by more than kLazyRescale
-        // (base-2 units).  Weights therefore stay below 2^kLazyRescale, and
-        // the common sub-tile needs no exchange between the row groups.  The
-        // first valid score of a column always raises its reference.
-        if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazyRescale) != 0) {
-            float cm = fmaxf(tmax, xor16(tmax));
-            cm = fmaxf(cm, xor32(cm, lane));
-            const float m_new = fmaxf(m_run, cm);
-            const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
-            l_run *= alpha;
-            static_for<0, DL>([&]<int e>() { acc[e] *= alpha; });
-            m_run = m_new;
-        }
-        const float mu = m_run == kNegInf ? 0.f : m_run;
-        float p[4];
-        static_for<0, 4>([&]<int r>() { p[r] = fast_exp2(sv[r] - mu); });
-        l_run += (p[0] + p[1]) + (p[2] + p[3]);
-        if constexpr (std::is_same_v<DT, BF16>) {
-            u32x2 ph, pl;
-            split_probs_bf16(p, ph, pl);
-            static_for<0, DL>([&]<int e>() {
-                const u32x2 av = {v_half<e>(vr[0]) | (v_half<e>(vr[1]) << 16),
-                                  v_half<e>(vr[2]) | (v_half<e>(vr[3]) << 16)};
-                acc[e] = mfma_pv<DT>(av, ph, acc[e]);
-                acc[e] = mfma_pv<DT>(av, pl, acc[e]);
-            });
-        } else {
-            const u32x2 pb = pack_probs_f16(p);
-            static_for<0, DL>([&]<int e>() {
-                const u32x2 av = {v_half<e>(vr[0]) | (v_half<e>(vr[1]) << 16),
-                                  v_half<e>(vr[2]) | (v_half<e>(vr[3]) << 16)};
-                acc[e] = mfma_pv<DT>(av, pb, acc[e]);
-            });
-        }
+        static_for<0, DL>([&]<int e>() {
+            const u32x2 av = {v_half<e>(vr[0]) | (v_half<e>(vr[1]) << 16),
+                              v_half<e>(vr[2]) | (v_half<e>(vr[3]) << 16)};
+            static_for<0, CH>([&]<int ch>() { acc[ch][e] = mfma_pv<DT>(av, ph[ch], acc[ch][e]); });
+            if constexpr (std::is_same_v<DT, BF16>) {
+                static_for<0, CH>([&]<int ch>() { acc[ch][e] = mfma_pv<DT>(av, pl[ch], acc[ch][e]); });
+            }
+        });
     };
 
     // ---- results.  A lane's dims in record / output order: (i, e) -> i * DL + e.
@@ -427,11 +440,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         x += xor16(x);
         return x + xor32(x, lane);
     };
-    // Writes (acc / l) for this lane's column, rounded to the output type.
-    auto write_final = [&](const f32x4 (&ac)[DL], float l) {
-        if (orow < 0) return;
+    // Writes (acc / l) of one column, rounded to the output type.
+    auto write_final = [&](int64_t row, const f32x4 (&ac)[DL], float l) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        char *o = static_cast<char *>(a.out) + orow * ROW + rg * DQ * EB;
+        char *o = static_cast<char *>(a.out) + row * ROW + rg * DQ * EB;
         static_for<0, 4>([&]<int i>() {
             float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             static_for<0, DL>([&]<int e>() { f[e] = ac[e][i] * inv; });
@@ -440,12 +452,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             else *reinterpret_cast<u32x2 *>(o + i * 8) = u32x2{pk[0], pk[1]};
         });
     };
-    // Stores a (max, exp-sum, acc) record of this lane's column: acc at
-    // racc + col * D, (max, sum) at rml + 2 * col.  Lanes of absent columns
-    // store nothing.
+    // Stores a (max, exp-sum, acc) record of one column: acc at racc + col * D,
+    // (max, sum) at rml + 2 * col.
     auto store_record = [&](float *racc, float *rml, int racc_bytes, int col, float m, float l,
                             const f32x4 (&ac)[DL], bool coherent) {
-        if (orow < 0) return;
         static_for<0, 4>([&]<int i>() {
             static_for<0, DL / 4>([&]<int v>() {
                 const f32x4 x = {ac[4 * v][i], ac[4 * v + 1][i], ac[4 * v + 2][i], ac[4 * v + 3][i]};
@@ -464,6 +474,14 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             }
         }
     };
+    // Stores this segment's record (all chunks) at `slot` of the record array.
+    auto store_segment = [&](int64_t slot, const float (&m)[CH], const float (&l)[CH], const f32x4 (&ac)[CH][DL]) {
+        float *ra = a.ws_acc + slot * kRecFloats;
+        float *rm = a.ws_ml + slot * UC * 2;
+        static_for<0, CH>([&]<int ch>() {
+            if (orow[ch] >= 0) store_record(ra, rm, 0, ch * kMultiCols + c, m[ch], l[ch], ac[ch], false);
+        });
+    };
     // Folds record (m2, l2, a2) into (m, l, ac), in that order.
     auto fold = [&](float &m, float &l, f32x4 (&ac)[DL], float m2, float l2, const f32x4 (&a2)[DL]) {
         const float mn = fmaxf(m, m2);
@@ -475,142 +493,58 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         });
         m = mn;
     };
-    // Merges records [first, first + cnt) into (m, l, ac), in index order.
-    // Per block of kMergeBlock records: their (max, sum) pairs in one round
-    // trip, then their acc rows one record after another.
-    // Absent columns load nothing (out-of-range offsets read as zero).
-    constexpr int kMergeBlock = 8;
-    auto merge = [&](const float *racc, const float *rml, int64_t first, int cnt, float &m, float &l,
-                     f32x4 (&ac)[DL]) {
-        m = kNegInf;
-        l = 0.f;
-        static_for<0, DL>([&]<int e>() { ac[e] = f32x4{0.f, 0.f, 0.f, 0.f}; });
-        const int aoff = orow >= 0 ? (c * D + rg * DQ) * 4 : 0x7FFFF000;
-        for (int r0 = 0; r0 < cnt; r0 += kMergeBlock) {
-            float mb[kMergeBlock], lb[kMergeBlock];
-            static_for<0, kMergeBlock>([&]<int b>() {
-                const int64_t rr = first + (r0 + b < cnt ? r0 + b : 0);
-                const float *rm = rml + rr * kMultiCols * 2 + 2 * c;
-                mb[b] = __hip_atomic_load(rm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                lb[b] = __hip_atomic_load(rm + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (r0 + b >= cnt) {
-                    mb[b] = kNegInf;
-                    lb[b] = 0.f;
-                }
-            });
-            float mn = m;
-            static_for<0, kMergeBlock>([&]<int b>() { mn = fmaxf(mn, mb[b]); });
-            const float mu = mn == kNegInf ? 0.f : mn;
-            const float x = fast_exp2(m - mu);
-            l *= x;
-            static_for<0, DL>([&]<int e>() { ac[e] *= x; });
-            float w[kMergeBlock];
-            static_for<0, kMergeBlock>([&]<int b>() {
-                w[b] = fast_exp2(mb[b] - mu);
-                l = __builtin_fmaf(w[b], lb[b], l);
-            });
-            m = mn;
-            static_for<0, kMergeBlock>([&]<int b>() {
-                if (r0 + b < cnt) {
-                    const float *ra = racc + (first + r0 + b) * kMultiCols * D;
-                    f32x4 xa[DL];
-                    static_for<0, DL>([&]<int q>() { xa[q] = load_coherent(ra, kMultiCols * D * 4, aoff + q * 16); });
-                    // acc element (i, e) sits at float i * DL + e of the lane's slice
-                    static_for<0, DL>([&]<int q>() {
-                        static_for<0, 4>([&]<int k>() {
-                            constexpr int fl = 4 * q + k, i = fl / DL, e = fl % DL;
-                            ac[e][i] = __builtin_fmaf(w[b], xa[q][k], ac[e][i]);
-                        });
-                    });
-                }
-            });
-        }
-    };
     // The unit's result: output (multi), output merged with the prefix
     // record (suffix), or the prefix record itself (prefix).
-    auto finalize = [&](const MCursor &u, float m, float l, f32x4 (&ac)[DL]) {
-        if (orow < 0) return;
-        if (mode == kModePrefix) {
-            store_record(a.pre_acc + orow * D, a.pre_ml + 2 * orow, 0, 0, m, l, ac, false);
-            return;
-        }
-        if (mode == kModeSuffix && u.lo > 0) {
-            f32x4 a2[DL];
-            const float *pa = a.pre_acc + orow * D + rg * DQ;
-            static_for<0, 4>([&]<int i>() {
-                static_for<0, DL / 4>([&]<int v>() {
-                    const f32x4 x = *reinterpret_cast<const f32x4 *>(pa + i * DL + 4 * v);
-                    static_for<0, 4>([&]<int k>() { a2[4 * v + k][i] = x[k]; });
+    auto finalize = [&](const MCursor &u, float (&m)[CH], float (&l)[CH], f32x4 (&ac)[CH][DL]) {
+        static_for<0, CH>([&]<int ch>() {
+            const int64_t row = orow[ch];
+            if (row < 0) return;
+            if (mode == kModePrefix) {
+                store_record(a.pre_acc + row * D, a.pre_ml + 2 * row, 0, 0, m[ch], l[ch], ac[ch], false);
+                return;
+            }
+            if (mode == kModeSuffix && u.lo > 0) {
+                f32x4 a2[DL];
+                const float *pa = a.pre_acc + row * D + rg * DQ;
+                static_for<0, 4>([&]<int i>() {
+                    static_for<0, DL / 4>([&]<int v>() {
+                        const f32x4 x = *reinterpret_cast<const f32x4 *>(pa + i * DL + 4 * v);
+                        static_for<0, 4>([&]<int k>() { a2[4 * v + k][i] = x[k]; });
+                    });
                 });
-            });
-            fold(m, l, ac, a.pre_ml[2 * orow], a.pre_ml[2 * orow + 1], a2);
-        }
-        write_final(ac, l);
+                fold(m[ch], l[ch], ac[ch], a.pre_ml[2 * row], a.pre_ml[2 * row + 1], a2);
+            }
+            write_final(row, ac[ch], l[ch]);
+        });
     };
 
-    auto arrive = [&](int32_t *ctr) {
-        wait_vmem_done();
-        int old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return __builtin_amdgcn_readlane(old, 0);
-    };
-    auto reset = [&](int32_t *ctr) {
-        if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-
-    // Leaves the unit at `u` after sub-tile `g_last`.  A unit split between
-    // k waves is merged by the last to arrive: directly for k <= 8, else in
-    // two levels (groups of about sqrt(k) consecutive records first).  The
-    // merge and the final write each have one call site, which keeps the
-    // register footprint of the kernel down.
+    // Leaves the unit at `u` after sub-tile `g_last`.  A unit inside this
+    // wave's range is finished here.  A unit split between k waves leaves k
+    // records (one per wave, at slot wave + unit) that the reduce pass merges
+    // after this launch; the wave holding the unit's first sub-tile describes
+    // the unit for it (first slot, k, row, KV head, chunk).
     auto finish_unit = [&](const MCursor &u, int g_last) {
-        float l = column_sum(l_run);
-        float m = m_run;
+        float m[CH], l[CH];
+        static_for<0, CH>([&]<int ch>() {
+            l[ch] = column_sum(l_run[ch]);
+            m[ch] = m_run[ch];
+        });
         const int ua = unit_first(u);
         const int ub = ua + u.n;
-        if (!(seg_first == ua && g_last + 1 == ub)) {
-            const int w_first = wave_of(ua);
-            const int w_last = wave_of(ub - 1);
-            const int k = w_last - w_first + 1;
-            const int unit = unit_index(u);
-            const int64_t base = (int64_t)w_first + unit;
-            const int64_t slot = (int64_t)wave + unit;
-            store_record(a.ws_acc + slot * kMultiCols * D, a.ws_ml + slot * kMultiCols * 2, kMultiCols * D * 4,
-                         c, m, l, acc, true);
-            const float *racc = a.ws_acc;
-            const float *rml = a.ws_ml;
-            int64_t first = base;
-            int cnt = k;
-            int ng = 0;              // groups of the second level (0: one level)
-            int64_t gslot = 0;
-            if (k <= kMDirectMerge) {
-                if (arrive(a.ws_cnt + unit) != k - 1) return;
-            } else {
-                int f1 = (int)__builtin_sqrtf((float)k);
-                while (f1 * f1 < k) ++f1;
-                ng = (k + f1 - 1) / f1;
-                const int j = (wave - w_first) / f1;
-                cnt = min(f1, k - j * f1);
-                first = base + (int64_t)j * f1;
-                gslot = base + j;
-                if (arrive(a.ws_gcnt + gslot) != cnt - 1) return;
-            }
-            while (true) {
-                merge(racc, rml, first, cnt, m, l, acc);
-                if (ng == 0) break;
-                store_record(a.ws_gacc + gslot * kMultiCols * D, a.ws_gml + gslot * kMultiCols * 2,
-                             kMultiCols * D * 4, c, m, l, acc, true);
-                reset(a.ws_gcnt + gslot);
-                if (arrive(a.ws_cnt + unit) != ng - 1) return;
-                racc = a.ws_gacc;
-                rml = a.ws_gml;
-                first = base;
-                cnt = ng;
-                ng = 0;
-            }
-            reset(a.ws_cnt + unit);
+        const int unit = unit_index(u);
+        const bool whole = seg_first == ua && g_last + 1 == ub;
+        if (seg_first == ua && lane == 0) {
+            const int k = whole ? 1 : wave_of(ub - 1) - wave + 1;
+            typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+            int32_t *d = a.unit_desc + kDescWords * (1 + (int64_t)unit);
+            *reinterpret_cast<i32x4 *>(d) = i32x4{wave + unit, k, u.row, (u.kvh << 16) | u.chunk};
+            *reinterpret_cast<i32x4 *>(d + 4) = i32x4{u.tseq, u.cols, u.lo, 0};
         }
-        finalize(u, m, l, acc);
+        if (whole) {
+            finalize(u, m, l, acc);
+            return;
+        }
+        store_segment((int64_t)wave + unit, m, l, acc);
     };
 
     // ---- main loop over [g0, g1), one outer iteration per segment, kMDepth
@@ -659,29 +593,173 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         if (g + 1 >= g1) break;
         advance(cp);
         ++g;
-        // the next sub-tile sits in buffer (brk + 1) % 2: bring it to buffer 0
-        static_assert(kMDepth == 2, "buffer rotation written for two buffers");
-        if (brk == 0) {
-            static_for<0, NLK>([&]<int e>() { kbuf[0][e] = kbuf[1][e]; });
-            static_for<0, 4>([&]<int e>() { vbuf[0][e] = vbuf[1][e]; });
+        // the next sub-tiles sit in buffers brk + 1, brk + 2, ... (mod kMDepth):
+        // bring them to buffers 0, 1, ...
+        if constexpr (kMDepth == 2) {
+            if (brk == 0) {
+                static_for<0, NLK>([&]<int e>() { kbuf[0][e] = kbuf[1][e]; });
+                static_for<0, 4>([&]<int e>() { vbuf[0][e] = vbuf[1][e]; });
+            }
+        } else {
+            static_for<0, kMDepth - 1>([&]<int b>() {
+                if (brk == b) {
+                    u32x4 tk[kMDepth][NLK];
+                    VReg tv[kMDepth][4];
+                    static_for<0, kMDepth>([&]<int m>() {
+                        static_for<0, NLK>([&]<int e>() { tk[m][e] = kbuf[m][e]; });
+                        static_for<0, 4>([&]<int e>() { tv[m][e] = vbuf[m][e]; });
+                    });
+                    static_for<0, kMDepth - 1>([&]<int m>() {
+                        constexpr int from = (b + 1 + m) % kMDepth;
+                        static_for<0, NLK>([&]<int e>() { kbuf[m][e] = tk[from][e]; });
+                        static_for<0, 4>([&]<int e>() { vbuf[m][e] = tv[from][e]; });
+                    });
+                }
+            });
         }
     }
 }
 
-template <typename DT, int D>
+// Merges the records of every unit the main pass split, and writes the
+// unit's result as the main pass would have.  One workgroup per unit at a
+// time; thread t owns column t % 16 of each chunk and dims
+// [(t / 16) * D / 16, (t / 16 + 1) * D / 16).  The (max, sum) pairs of up to
+// kReduceBatch records are loaded together, then their acc slices together,
+// and folded in record order.
+constexpr int kReduceThreads = 256;
+constexpr int kMaxReduceGroups = 2048;
+constexpr int kReduceBatch = 16;
+
+template <typename DT, int D, int CH>
+__global__ __launch_bounds__(kReduceThreads) void attn_multi_reduce(MultiArgs a) {
+    constexpr int UC = kMultiCols * CH;
+    constexpr int kRecFloats = UC * D;
+    constexpr int DPT = D / 16;          // dims per thread (4 or 8)
+    constexpr int NV = DPT / 4;          // float4s per thread and record
+    const int t = threadIdx.x;
+    const int c = t & 15;
+    const int d0 = (t >> 4) * DPT;
+    const int units = a.unit_desc[0];
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int32_t *d = a.unit_desc + kDescWords * (1 + (int64_t)unit);
+        const i32x4 dsc = *reinterpret_cast<const i32x4 *>(d);
+        const int64_t base = dsc[0];
+        const int k = dsc[1];
+        if (k <= 1) continue;
+        const i32x4 dsc2 = *reinterpret_cast<const i32x4 *>(d + 4);
+        const int row = dsc[2], kvh = dsc[3] >> 16, chunk = dsc[3] & 0xFFFF;
+        RowInfo ri{};
+        ri.tseq = dsc2[0];
+        ri.cols = dsc2[1];
+        ri.lo = dsc2[2];
+        for (int ch = 0; ch < CH; ++ch) {
+            const int col = ch * kMultiCols + c;
+            const int64_t orow = column_row(a, row, ri, kvh, (chunk * CH + ch) * kMultiCols + c);
+            if (orow < 0) continue;
+            float m = kNegInf, l = 0.f;
+            f32x4 acc[NV];
+            for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int r0 = 0; r0 < k; r0 += kReduceBatch) {
+                const int nb = min(kReduceBatch, k - r0);
+                float mb[kReduceBatch], lb[kReduceBatch];
+                f32x4 xb[kReduceBatch][NV];
+#pragma unroll
+                for (int b = 0; b < kReduceBatch; ++b) {
+                    if (b < nb) {
+                        const int64_t slot = base + r0 + b;
+                        mb[b] = a.ws_ml[(slot * UC + col) * 2];
+                        lb[b] = a.ws_ml[(slot * UC + col) * 2 + 1];
+                        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.ws_acc + slot * kRecFloats + col * D + d0);
+#pragma unroll
+                        for (int v = 0; v < NV; ++v) xb[b][v] = src[v];
+                    }
+                }
+                float mn = m;
+#pragma unroll
+                for (int b = 0; b < kReduceBatch; ++b) mn = b < nb ? fmaxf(mn, mb[b]) : mn;
+                const float mu = mn == kNegInf ? 0.f : mn;
+                const float x = fast_exp2(m - mu);
+                l *= x;
+                for (int v = 0; v < NV; ++v) acc[v] *= x;
+#pragma unroll
+                for (int b = 0; b < kReduceBatch; ++b) {
+                    if (b < nb) {
+                        const float w = fast_exp2(mb[b] - mu);
+                        l = __builtin_fmaf(w, lb[b], l);
+#pragma unroll
+                        for (int v = 0; v < NV; ++v) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[v][e] = __builtin_fmaf(w, xb[b][v][e], acc[v][e]);
+                        }
+                    }
+                }
+                m = mn;
+            }
+            if (a.mode == kModePrefix) {
+                f32x4 *dst = reinterpret_cast<f32x4 *>(a.pre_acc + orow * D + d0);
+                for (int v = 0; v < NV; ++v) dst[v] = acc[v];
+                if (t < 16) {
+                    a.pre_ml[2 * orow] = m;
+                    a.pre_ml[2 * orow + 1] = l;
+                }
+                continue;
+            }
+            if (a.mode == kModeSuffix && ri.lo > 0) {
+                const float m2 = a.pre_ml[2 * orow], l2 = a.pre_ml[2 * orow + 1];
+                const f32x4 *pa = reinterpret_cast<const f32x4 *>(a.pre_acc + orow * D + d0);
+                const float mn = fmaxf(m, m2);
+                const float mu = mn == kNegInf ? 0.f : mn;
+                const float x = fast_exp2(m - mu), y = fast_exp2(m2 - mu);
+                l = l * x + l2 * y;
+                for (int v = 0; v < NV; ++v) {
+                    const f32x4 p2 = pa[v];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[v][e] = __builtin_fmaf(p2[e], y, acc[v][e] * x);
+                }
+            }
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f[4 * v + e] = acc[v][e] * inv;
+            }
+            const u32x4 pk = pack_chunk<DT>(f);
+            char *o = static_cast<char *>(a.out) + orow * (D * 2) + d0 * 2;
+            if constexpr (DPT == 8) *reinterpret_cast<u32x4 *>(o) = pk;
+            else *reinterpret_cast<u32x2 *>(o) = u32x2{pk[0], pk[1]};
+        }
+    }
+}
+
+template <typename DT, int D, int CH>
 hipError_t launch_multi_typed(const MultiArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.num_waves / kWavesPerGroup));
-    attn_multi_kernel<DT, D><<<grid, dim3(kWavesPerGroup * kWave), 0, stream>>>(a);
+    attn_multi_kernel<DT, D, CH><<<grid, dim3(kWavesPerGroup * kWave), 0, stream>>>(a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    // the reduce pass: enough workgroups to cover the split units quickly
+    const int groups = a.max_units < kMaxReduceGroups ? a.max_units : kMaxReduceGroups;
+    attn_multi_reduce<DT, D, CH><<<dim3((unsigned)(groups > 0 ? groups : 1)), dim3(kReduceThreads), 0, stream>>>(a);
     return hipGetLastError();
 }
 
-template <typename DT, int D>
+template <typename DT, int D, int CH>
 int multi_waves_typed() {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_multi_kernel<DT, D>, kWavesPerGroup * kWave, 0) !=
-        hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_multi_kernel<DT, D, CH>, kWavesPerGroup * kWave,
+                                                     0) != hipSuccess)
         return 0;
     return blocks * kWavesPerGroup;
+}
+
+template <typename DT, int D>
+hipError_t launch_multi_chunks(int chunks, const MultiArgs &a, hipStream_t stream) {
+    return chunks == 2 ? launch_multi_typed<DT, D, 2>(a, stream) : launch_multi_typed<DT, D, 1>(a, stream);
+}
+template <typename DT, int D>
+int multi_waves_chunks(int chunks) {
+    return chunks == 2 ? multi_waves_typed<DT, D, 2>() : multi_waves_typed<DT, D, 1>();
 }
 
 }  // namespace
@@ -690,24 +768,27 @@ bool multi_supported(int32_t dtype, int32_t head_dim) {
     return (dtype == 1 || dtype == 2) && (head_dim == 64 || head_dim == 128);
 }
 
-int multi_waves_per_cu(int32_t dtype, int32_t head_dim) {
-    static std::atomic<int> cache[2][2];
-    if (!multi_supported(dtype, head_dim)) return 0;
+int multi_waves_per_cu(int32_t dtype, int32_t head_dim, int32_t chunks) {
+    static std::atomic<int> cache[2][2][kMultiChunksMax];
+    if (!multi_supported(dtype, head_dim) || chunks < 1 || chunks > kMultiChunksMax) return 0;
     const int di = dtype - 1, hi = head_dim == 128 ? 1 : 0;
-    int v = cache[di][hi].load(std::memory_order_relaxed);
+    int v = cache[di][hi][chunks - 1].load(std::memory_order_relaxed);
     if (v > 0) return v;
-    if (dtype == 1) v = head_dim == 128 ? multi_waves_typed<F16, 128>() : multi_waves_typed<F16, 64>();
-    else v = head_dim == 128 ? multi_waves_typed<BF16, 128>() : multi_waves_typed<BF16, 64>();
-    if (v > 0) cache[di][hi].store(v, std::memory_order_relaxed);
+    if (dtype == 1) v = head_dim == 128 ? multi_waves_chunks<F16, 128>(chunks) : multi_waves_chunks<F16, 64>(chunks);
+    else v = head_dim == 128 ? multi_waves_chunks<BF16, 128>(chunks) : multi_waves_chunks<BF16, 64>(chunks);
+    if (v > 0) cache[di][hi][chunks - 1].store(v, std::memory_order_relaxed);
     return v;
 }
 
-hipError_t launch_attn_multi(int32_t dtype, int32_t head_dim, const MultiArgs &a, hipStream_t stream) {
+hipError_t launch_attn_multi(int32_t dtype, int32_t head_dim, int32_t chunks, const MultiArgs &a,
+                             hipStream_t stream) {
     if (dtype == 1) {
-        return head_dim == 128 ? launch_multi_typed<F16, 128>(a, stream) : launch_multi_typed<F16, 64>(a, stream);
+        return head_dim == 128 ? launch_multi_chunks<F16, 128>(chunks, a, stream)
+                               : launch_multi_chunks<F16, 64>(chunks, a, stream);
     }
     if (dtype == 2) {
-        return head_dim == 128 ? launch_multi_typed<BF16, 128>(a, stream) : launch_multi_typed<BF16, 64>(a, stream);
+        return head_dim == 128 ? launch_multi_chunks<BF16, 128>(chunks, a, stream)
+                               : launch_multi_chunks<BF16, 64>(chunks, a, stream);
     }
     return hipErrorInvalidValue;
 }

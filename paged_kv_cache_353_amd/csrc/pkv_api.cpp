@@ -239,14 +239,18 @@ int multi_checks(const void *out, const void *q, const void *k_cache, const void
     return PKV_OK;
 }
 
-int multi_waves(int32_t dtype, int32_t head_dim, int64_t *waves) {
+// Column chunks a unit streams together: two when rows have more than 16
+// query columns per KV head (each K/V tile is then loaded once for 32).
+int32_t chunks_for(int64_t cols) { return cols > pkv::kMultiCols ? 2 : 1; }
+
+int multi_waves(int32_t dtype, int32_t head_dim, int32_t chunks, int64_t *waves) {
     int device = 0, cus = 0;
     if (hipGetDevice(&device) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
         return PKV_ERR_HIP;
-    int per_cu = pkv::multi_waves_per_cu(dtype, head_dim);
+    int per_cu = pkv::multi_waves_per_cu(dtype, head_dim, chunks);
     if (per_cu <= 0 || cus <= 0) return PKV_ERR_HIP;
-    per_cu = per_cu < 4 * pkv::kWavesPerSimd ? per_cu : 4 * pkv::kWavesPerSimd;
+    per_cu = per_cu < 4 * pkv::kMultiWavesPerSimd ? per_cu : 4 * pkv::kMultiWavesPerSimd;
     int64_t w = (int64_t)cus * per_cu;
     w = w < pkv::kMaxWaves ? w : pkv::kMaxWaves;
     w -= w % pkv::kWavesPerGroup;
@@ -256,12 +260,9 @@ int multi_waves(int32_t dtype, int32_t head_dim, int64_t *waves) {
 
 void fill_multi_split(pkv::MultiArgs &a, const pkv::MultiWorkspace &ws, void *workspace) {
     char *w = static_cast<char *>(workspace);
-    a.ws_cnt = reinterpret_cast<int32_t *>(w + ws.split.cnt_offset);
-    a.ws_gcnt = reinterpret_cast<int32_t *>(w + ws.split.gcnt_offset);
-    a.ws_acc = reinterpret_cast<float *>(w + ws.split.acc_offset);
-    a.ws_ml = reinterpret_cast<float *>(w + ws.split.ml_offset);
-    a.ws_gacc = reinterpret_cast<float *>(w + ws.split.gacc_offset);
-    a.ws_gml = reinterpret_cast<float *>(w + ws.split.gml_offset);
+    a.unit_desc = reinterpret_cast<int32_t *>(w + ws.desc_offset);
+    a.ws_acc = reinterpret_cast<float *>(w + ws.acc_offset);
+    a.ws_ml = reinterpret_cast<float *>(w + ws.ml_offset);
     a.pre_acc = reinterpret_cast<float *>(w + ws.pre_acc_offset);
     a.pre_ml = reinterpret_cast<float *>(w + ws.pre_ml_offset);
 }
@@ -298,8 +299,9 @@ int paged_attn_decode_multi(void *out, const void *q, const void *k_cache, const
     const pkv::MultiWorkspace ws = pkv::multi_workspace(units, 0, head_dim);
     if (!workspace || workspace_bytes < ws.bytes) return PKV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
+    const int32_t chunks = chunks_for((int64_t)num_query_tokens * (num_q_heads / num_kv_heads));
     int64_t waves = 0;
-    if ((st = multi_waves(dtype, head_dim, &waves)) != PKV_OK) return st;
+    if ((st = multi_waves(dtype, head_dim, chunks, &waves)) != PKV_OK) return st;
     pkv::MultiArgs a{};
     a.out = out;
     a.q = q;
@@ -320,7 +322,7 @@ int paged_attn_decode_multi(void *out, const void *q, const void *k_cache, const
     a.max_context_len = max_context_len;
     a.num_waves = (int32_t)waves;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-    return pkv::launch_attn_multi(dtype, head_dim, a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    return pkv::launch_attn_multi(dtype, head_dim, chunks, a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 size_t paged_attn_decode_shared_workspace_size(int32_t num_seqs, int32_t num_groups, int32_t num_q_heads,
@@ -352,8 +354,13 @@ int paged_attn_decode_shared(void *out, const void *q, const void *k_cache, cons
     const pkv::MultiWorkspace ws = pkv::multi_workspace(units, (int64_t)num_seqs * num_q_heads, head_dim);
     if (!workspace || workspace_bytes < ws.bytes) return PKV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
-    int64_t waves = 0;
-    if ((st = multi_waves(dtype, head_dim, &waves)) != PKV_OK) return st;
+    // prefix rows have (members x group) columns: the mean group size decides
+    const int64_t G = num_q_heads / num_kv_heads;
+    const int32_t pre_chunks = chunks_for(((int64_t)num_seqs * G + num_groups - 1) / num_groups);
+    const int32_t suf_chunks = chunks_for(G);
+    int64_t pre_waves = 0, suf_waves = 0;
+    if ((st = multi_waves(dtype, head_dim, pre_chunks, &pre_waves)) != PKV_OK) return st;
+    if ((st = multi_waves(dtype, head_dim, suf_chunks, &suf_waves)) != PKV_OK) return st;
     pkv::MultiArgs a{};
     a.out = out;
     a.q = q;
@@ -372,16 +379,17 @@ int paged_attn_decode_shared(void *out, const void *q, const void *k_cache, cons
     a.block_shift = log2_exact(block_size);
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_context_len = max_context_len;
-    a.num_waves = (int32_t)waves;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
     // the shared prefix of every group once for all its members, then each
     // sequence's own suffix merged with its prefix record (stream order)
     a.mode = pkv::kModePrefix;
     a.num_rows = num_groups;
-    if (pkv::launch_attn_multi(dtype, head_dim, a, stream) != hipSuccess) return PKV_ERR_HIP;
+    a.num_waves = (int32_t)pre_waves;
+    if (pkv::launch_attn_multi(dtype, head_dim, pre_chunks, a, stream) != hipSuccess) return PKV_ERR_HIP;
     a.mode = pkv::kModeSuffix;
     a.num_rows = num_seqs;
-    return pkv::launch_attn_multi(dtype, head_dim, a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    a.num_waves = (int32_t)suf_waves;
+    return pkv::launch_attn_multi(dtype, head_dim, suf_chunks, a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 int paged_attn_decode(void *out, const void *q, const void *k_cache, const void *v_cache,

@@ -125,7 +125,12 @@ enum MultiMode : int32_t {
                       // writes one (max, exp-sum, acc) record per (sequence, q head)
     kModeSuffix = 2,  // rows = sequences; tokens [P, L); columns = heads; folds in the record
 };
-constexpr int kMultiCols = 16;  // query columns per unit (the MFMA's N)
+constexpr int kMultiCols = 16;  // query columns per chunk (the MFMA's N)
+constexpr int kMultiChunksMax = 2;  // column chunks a unit streams together (one K/V load)
+// Resident waves per SIMD the many-column grid is sized for.  With two, the
+// younger wave of each SIMD streams at about 60% of the older one's rate and
+// the call ends on its tail; one wave per SIMD measured 15-25% faster.
+constexpr int kMultiWavesPerSimd = 1;
 
 struct MultiArgs {
     void *out;
@@ -138,12 +143,11 @@ struct MultiArgs {
     const int32_t *prefix_lens;   // shared modes: [num_seqs]
     float *pre_acc;               // shared modes: [num_seqs * num_q_heads][head_dim]
     float *pre_ml;                // shared modes: [num_seqs * num_q_heads][2]
-    int32_t *ws_cnt;
-    int32_t *ws_gcnt;
-    float *ws_acc;                // [kMaxWaves + units][kMultiCols][head_dim]
-    float *ws_ml;                 // [kMaxWaves + units][kMultiCols][2]
-    float *ws_gacc;
-    float *ws_gml;
+    int32_t *unit_desc;           // [0]: units of the call; then 8 int32 per unit (from word 8):
+                                  // first record slot, records, row, (KV head << 16) | chunk,
+                                  // table sequence, columns, first attended position, 0
+    float *ws_acc;                // [kMaxWaves + units][columns of a unit][head_dim] partial records
+    float *ws_ml;                 // [kMaxWaves + units][columns of a unit][2]
     int32_t mode;
     int32_t num_rows;             // sequences, or groups in the prefix mode
     int32_t num_seqs;
@@ -158,8 +162,13 @@ struct MultiArgs {
     float scale_log2;
 };
 
+// Workspace of the many-column kernels.  The counter region of the
+// single-query decode is left in place (and untouched), so one workspace can
+// serve both kinds of call.
 struct MultiWorkspace {
-    DecodeWorkspace split;   // counters and partial records, sized for kMultiCols columns
+    size_t desc_offset;      // unit descriptors
+    size_t acc_offset;       // partial records
+    size_t ml_offset;
     size_t pre_acc_offset;   // prefix records (shared modes)
     size_t pre_ml_offset;
     size_t bytes;
@@ -167,17 +176,22 @@ struct MultiWorkspace {
 
 inline MultiWorkspace multi_workspace(int64_t max_units, int64_t pre_records, int32_t head_dim) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t slots = (size_t)kMaxWaves + (size_t)max_units;
+    const size_t cols = (size_t)kMultiCols * kMultiChunksMax;   // a record holds every column of a unit
     MultiWorkspace w{};
-    // decode_workspace sizes its slots for num_seqs * num_kv_heads units
-    w.split = decode_workspace((int32_t)max_units, 1, kMultiCols, head_dim);
-    w.pre_acc_offset = w.split.bytes;
+    w.desc_offset = up(kCounterBytes);
+    w.acc_offset = w.desc_offset + up((8 + 8 * (size_t)max_units) * sizeof(int32_t));
+    w.ml_offset = w.acc_offset + up(slots * cols * (size_t)head_dim * sizeof(float));
+    w.pre_acc_offset = w.ml_offset + up(slots * cols * 2 * sizeof(float));
     w.pre_ml_offset = w.pre_acc_offset + up((size_t)pre_records * (size_t)head_dim * sizeof(float));
     w.bytes = w.pre_ml_offset + up((size_t)pre_records * 2 * sizeof(float));
     return w;
 }
 
 bool multi_supported(int32_t dtype, int32_t head_dim);
-int multi_waves_per_cu(int32_t dtype, int32_t head_dim);
-hipError_t launch_attn_multi(int32_t dtype, int32_t head_dim, const MultiArgs &a, hipStream_t stream);
+int multi_waves_per_cu(int32_t dtype, int32_t head_dim, int32_t chunks);
+// chunks: column chunks per unit (1 or 2), chosen by the caller from the columns a row has
+hipError_t launch_attn_multi(int32_t dtype, int32_t head_dim, int32_t chunks, const MultiArgs &a,
+                             hipStream_t stream);
 
 }  // namespace pkv

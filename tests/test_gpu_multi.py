@@ -40,7 +40,7 @@ def check_multi(inp, q4, triples=None, what=""):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv,T", [(8, 8, 1), (8, 2, 1), (8, 2, 3), (16, 2, 2), (4, 2, 8),
-                                      (2, 2, 16), (8, 2, 5), (16, 1, 2), (6, 2, 7)])
+                                      (2, 2, 16), (8, 2, 5), (16, 1, 2), (6, 2, 7), (8, 2, 16)])
 def test_multi_small_shapes(dtype, D, Hq, Hkv, T):
     say(f"case: multi dtype={dtype} D={D} Hq={Hq} Hkv={Hkv} T={T}")
     lens = [0, 1, T, 15, 16, 17, 250, 1000]
