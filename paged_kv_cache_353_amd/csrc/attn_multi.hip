@@ -5,11 +5,12 @@
 //    draft verification produce them), each attending to every position up
 //    to its own: the new tokens are the last T positions of the sequence;
 //  * forks whose Block Tables point at the same physical blocks for a common
-//    prefix ("PagedAttention核心思想" section 2.4.3): the prefix is streamed
-//    once for all forks of a group, then each fork streams its own suffix and
-//    the two partial results are merged.
-// Either way one K/V tile serves up to 16 query columns, which turns both
-// products of the tile into matrix-core work:
+//    prefix ("PagedAttention核心思想" section 2.4.3): the prefix of a group is
+//    streamed once for the query heads of all its members, each member's own
+//    suffix separately, and the two partial results are merged.
+// Either way one K/V tile serves up to 16 query columns per chunk (two
+// chunks per unit), which turns both products of the tile into matrix-core
+// work:
 //  * scores S = K q^T: one 16x16x32 MFMA per 32 dims, tokens as rows and
 //    query columns as columns (lane (r, j) receives tokens 4r..4r+3 of
 //    column j);
@@ -25,13 +26,14 @@
 // so most sub-tiles need no exchange between the lanes of a column.
 //
 // Work split and masking follow the single-query kernel: every (row, KV head,
-// column chunk) unit is cut into 16-token sub-tiles, and all sub-tiles are
-// shared out in equal contiguous ranges, one per resident wave.  A unit split
-// between k waves leaves k partial records; a second, short launch merges
-// them, every record of a unit in flight at once, in a fixed order.  Loads use
-// descriptors that span only the unit's valid rows, so rows past the end read
-// as zero, and every score outside a column's window is set to -inf before the
-// exponential, so stale cache contents never reach the result.
+// column chunks) unit is cut into 16-token sub-tiles, and all sub-tiles are
+// shared out in equal contiguous ranges, one per resident wave.  Units split
+// between waves, and in the shared-prefix case every unit, leave partial
+// records; a second, short launch merges them in a fixed order with every
+// record of an output in flight at once.  Loads use descriptors that span
+// only the unit's valid rows, so rows past the end read as zero, and every
+// score outside a column's window is set to -inf before the exponential, so
+// stale cache contents never reach the result.
 #include "pkv_device.h"
 
 #include <atomic>
@@ -45,11 +47,13 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMDepth = 2;        // sub-tiles in flight per wave
 constexpr int kDescWords = 8;     // unit descriptor: first slot, records, row, kvh|chunk, tseq, cols, lo, -
+constexpr int kColDescWords = 4;  // column descriptor: first slot, records, column in the record, flags
+constexpr int kHasPrefix = 1;     // flag of a suffix column descriptor: a prefix part exists
 constexpr float kLazyRescale = 8.f;  // headroom of the softmax reference (weights < 2^8)
 
 // Position of a wave's load or compute stage.  Every field is wave-uniform.
 struct MCursor {
-    int row;     // sequence, or group in the prefix mode
+    int row;     // sequence, or (shared mode) group or sequence
     int kvh;     // KV head
     int chunk;   // column chunk
     int sub;     // sub-tile inside the unit
@@ -61,6 +65,7 @@ struct MCursor {
     int L;       // the row's sequence length (multi mode: the query window's end)
     int tseq;    // sequence whose Block Table the row walks
     int cols;    // query columns of the row, per KV head
+    int kind;    // kRowMulti, kRowPrefix or kRowSuffix
     int pre;     // sub-tiles of all rows before this one
     int upre;    // units of all rows before this one
 };
@@ -115,10 +120,13 @@ __device__ __forceinline__ uint32_t v_half(const VR &v) {
 }
 
 // A row of the many-column kernel: the token range it streams, the first
-// position its columns attend, its length, the sequence whose table it walks
-// and its query columns per KV head.  `ld` reads a 32-bit entry of a length
-// array (scalar or vector loads).
-struct RowInfo { int t0, tend, lo, L, tseq, cols; };
+// position its columns attend, its length, the sequence whose table it walks,
+// its query columns per KV head and its kind.  In the shared mode rows
+// [0, num_groups) are the groups' prefixes and the rest the sequences'
+// suffixes.  `ld` reads a 32-bit entry of a length array (scalar or vector
+// loads).
+enum RowKind : int { kRowMulti = 0, kRowPrefix = 1, kRowSuffix = 2 };
+struct RowInfo { int t0, tend, lo, L, tseq, cols, kind; };
 
 template <typename LD>
 __device__ __forceinline__ RowInfo row_info_of(const MultiArgs &a, int r, LD ld) {
@@ -126,41 +134,46 @@ __device__ __forceinline__ RowInfo row_info_of(const MultiArgs &a, int r, LD ld)
     const int Lmax = a.max_context_len;
     auto clampL = [&](int L) { L = L < Lmax ? L : Lmax; return L > 0 ? L : 0; };
     RowInfo ri{};
-    if (a.mode == kModePrefix) {
+    if (a.mode == kModeShared && r < a.num_groups) {
         // members clamped to the batch (the description is device data)
         int f = ld(a.group_starts, r), e = ld(a.group_starts, r + 1);
         f = min(max(f, 0), a.num_seqs);
         e = min(max(e, f), a.num_seqs);
-        const int P = clampL(ld(a.prefix_lens, f));
-        ri.t0 = 0; ri.tend = P; ri.lo = 0; ri.L = P; ri.tseq = f; ri.cols = (e - f) * G;
-    } else if (a.mode == kModeSuffix) {
-        const int L = clampL(ld(a.context_lens, r));
-        int P = clampL(ld(a.prefix_lens, r));
+        const int P = f < e ? clampL(ld(a.prefix_lens, f)) : 0;
+        ri.t0 = 0; ri.tend = P; ri.lo = 0; ri.L = P; ri.tseq = f; ri.cols = (e - f) * G; ri.kind = kRowPrefix;
+    } else if (a.mode == kModeShared) {
+        const int i = r - a.num_groups;
+        const int L = clampL(ld(a.context_lens, i));
+        int P = clampL(ld(a.prefix_lens, i));
         P = P < L ? P : L;
-        // an empty suffix streams nothing (its output is the prefix record)
-        ri.t0 = P < L ? (P & ~15) : P; ri.tend = L; ri.lo = P; ri.L = L; ri.tseq = r; ri.cols = G;
+        // an empty suffix streams nothing (its output is the prefix part alone)
+        ri.t0 = P < L ? (P & ~15) : P; ri.tend = L; ri.lo = P; ri.L = L; ri.tseq = i; ri.cols = G;
+        ri.kind = kRowSuffix;
     } else {
         const int L = clampL(ld(a.context_lens, r));
         ri.t0 = 0; ri.tend = L; ri.lo = 0; ri.L = L; ri.tseq = r; ri.cols = a.num_query_tokens * G;
+        ri.kind = kRowMulti;
     }
     return ri;
 }
 
 // Output row of column x (0-based within its row) of KV head kvh, or -1 if
-// the row has no such column: an index into out ([.., Hq, D] rows) in the
-// multi and suffix modes, into the prefix records in the prefix mode.
+// the row has no such column.  Multi mode: a row of out
+// [num_seqs, num_query_tokens, Hq, D]; shared mode: the (sequence, q head)
+// item, a row of out [num_seqs, Hq, D].  The query of the column is the same
+// row of q.
 __device__ __forceinline__ int64_t column_row(const MultiArgs &a, int row, const RowInfo &ri, int kvh, int x) {
     if (x >= ri.cols) return -1;
     const int Hq = a.num_q_heads, G = Hq / a.num_kv_heads;
-    if (a.mode == kModeMulti) {
+    if (ri.kind == kRowMulti) {
         const int jq = x / G, h = x - jq * G;
         return ((int64_t)row * a.num_query_tokens + jq) * Hq + kvh * G + h;
     }
-    if (a.mode == kModePrefix) {
+    if (ri.kind == kRowPrefix) {
         const int mem = x / G, h = x - mem * G;
         return (int64_t)(ri.tseq + mem) * Hq + kvh * G + h;
     }
-    return (int64_t)row * Hq + kvh * G + x;
+    return (int64_t)ri.tseq * Hq + kvh * G + x;
 }
 
 template <typename DT, int D, int CH>
@@ -193,28 +206,21 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     auto tiles_of = [&](const RowInfo &ri) { return (ri.tend - ri.t0 + 15) >> 4; };
     auto chunks_of = [&](const RowInfo &ri) { return (ri.cols + UC - 1) / UC; };
 
-    // ---- rows with nothing to stream: zero outputs, or (suffix mode) the
-    // prefix record on its own
-    if (mode != kModePrefix) {
-        for (int r = wave; r < R; r += W) {
-            const RowInfo ri = row_info(r, ld_scalar);
-            if (ri.tend - ri.t0 > 0) continue;
-            // here L == 0 (multi) or the suffix is empty (suffix mode)
-            const int nrow = mode == kModeMulti ? Tq * Hq : Hq;
-            char *o = static_cast<char *>(a.out) + (int64_t)r * nrow * ROW;
-            for (int idx = lane; idx < nrow * (ROW / 16); idx += kWave) {
-                const int h = idx / (ROW / 16), ch = idx - h * (ROW / 16);
-                u32x4 z = {0u, 0u, 0u, 0u};
-                if (mode == kModeSuffix && ri.lo > 0) {
-                    const int64_t rec = (int64_t)r * Hq + h;
-                    const float l = a.pre_ml[2 * rec + 1];
-                    const float inv = l > 0.f ? 1.f / l : 0.f;
-                    float f[8];
-                    for (int e = 0; e < 8; ++e) f[e] = a.pre_acc[rec * D + ch * 8 + e] * inv;
-                    z = pack_chunk<DT>(f);
-                }
-                *reinterpret_cast<u32x4 *>(o + (int64_t)h * ROW + ch * 16) = z;
-            }
+    // ---- rows with nothing to stream.  Multi mode: zero outputs.  Shared
+    // mode, a sequence whose suffix is empty: its column descriptors say so
+    // (its result is the prefix part alone, or zero).
+    for (int r = wave; r < R; r += W) {
+        const RowInfo ri = row_info(r, ld_scalar);
+        if (ri.tend - ri.t0 > 0 || ri.kind == kRowPrefix) continue;
+        if (ri.kind == kRowMulti) {
+            char *o = static_cast<char *>(a.out) + (int64_t)r * Tq * Hq * ROW;
+            for (int idx = lane; idx < Tq * Hq * (ROW / 16); idx += kWave)
+                *reinterpret_cast<u32x4 *>(o + (int64_t)idx * 16) = u32x4{0u, 0u, 0u, 0u};
+        } else {
+            typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+            for (int h = lane; h < Hq; h += kWave)
+                *reinterpret_cast<i32x4 *>(a.col_desc + kColDescWords * ((int64_t)ri.tseq * Hq + h)) =
+                    i32x4{0, 0, 0, ri.lo > 0 ? kHasPrefix : 0};
         }
     }
 
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     auto load_row = [&](MCursor &u) {
         const RowInfo ri = row_info(u.row, ld_scalar);
         u.t0 = uniform(ri.t0); u.tend = uniform(ri.tend); u.lo = uniform(ri.lo); u.L = uniform(ri.L);
-        u.tseq = uniform(ri.tseq); u.cols = uniform(ri.cols);
+        u.tseq = uniform(ri.tseq); u.cols = uniform(ri.cols); u.kind = uniform(ri.kind);
         u.n = uniform((u.tend - u.t0 + 15) >> 4);
         u.chunks = uniform((u.cols + UC - 1) / UC);
     };
@@ -351,24 +357,24 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     auto start_unit = [&](const MCursor &u) {
         int64_t qbase = 0;                          // first q row of the row
         int qspan = 0;                              // q rows of the row
-        if (mode == kModeMulti) {
+        if (u.kind == kRowMulti) {
             qbase = (int64_t)u.row * Tq * Hq;
             qspan = Tq * Hq;
-        } else if (mode == kModePrefix) {
+        } else if (u.kind == kRowPrefix) {
             qbase = (int64_t)u.tseq * Hq;
             qspan = (u.cols / G) * Hq;
         } else {
-            qbase = (int64_t)u.row * Hq;
+            qbase = (int64_t)u.tseq * Hq;
             qspan = Hq;
         }
-        const RowInfo ri{u.t0, u.tend, u.lo, u.L, u.tseq, u.cols};
+        const RowInfo ri{u.t0, u.tend, u.lo, u.L, u.tseq, u.cols, u.kind};
         const char *qb = static_cast<const char *>(a.q) + uniform(qbase * ROW);
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, uniform(qspan * ROW), kBufferFlags);
         static_for<0, CH>([&]<int ch>() {
             const int x = (u.chunk * CH + ch) * kMultiCols + c;   // column index within the row
             orow[ch] = column_row(a, u.row, ri, u.kvh, x);
             const bool valid = orow[ch] >= 0;
-            if (mode == kModeMulti) lim[ch] = valid ? u.L - Tq + x / G + 1 : 0;
+            if (u.kind == kRowMulti) lim[ch] = valid ? u.L - Tq + x / G + 1 : 0;
             else lim[ch] = valid ? u.L : 0;
             // q rows are the output rows (the prefix records are indexed the same way)
             const int qoff = valid ? (int)(orow[ch] - qbase) * ROW + 16 * rg : 0x7FFFFF00;   // out of range: zero
@@ -482,47 +488,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             if (orow[ch] >= 0) store_record(ra, rm, 0, ch * kMultiCols + c, m[ch], l[ch], ac[ch], false);
         });
     };
-    // Folds record (m2, l2, a2) into (m, l, ac), in that order.
-    auto fold = [&](float &m, float &l, f32x4 (&ac)[DL], float m2, float l2, const f32x4 (&a2)[DL]) {
-        const float mn = fmaxf(m, m2);
-        const float mu = mn == kNegInf ? 0.f : mn;
-        const float x = fast_exp2(m - mu), y = fast_exp2(m2 - mu);
-        l = l * x + l2 * y;
-        static_for<0, DL>([&]<int e>() {
-            static_for<0, 4>([&]<int i>() { ac[e][i] = __builtin_fmaf(a2[e][i], y, ac[e][i] * x); });
-        });
-        m = mn;
-    };
-    // The unit's result: output (multi), output merged with the prefix
-    // record (suffix), or the prefix record itself (prefix).
-    auto finalize = [&](const MCursor &u, float (&m)[CH], float (&l)[CH], f32x4 (&ac)[CH][DL]) {
-        static_for<0, CH>([&]<int ch>() {
-            const int64_t row = orow[ch];
-            if (row < 0) return;
-            if (mode == kModePrefix) {
-                store_record(a.pre_acc + row * D, a.pre_ml + 2 * row, 0, 0, m[ch], l[ch], ac[ch], false);
-                return;
-            }
-            if (mode == kModeSuffix && u.lo > 0) {
-                f32x4 a2[DL];
-                const float *pa = a.pre_acc + row * D + rg * DQ;
-                static_for<0, 4>([&]<int i>() {
-                    static_for<0, DL / 4>([&]<int v>() {
-                        const f32x4 x = *reinterpret_cast<const f32x4 *>(pa + i * DL + 4 * v);
-                        static_for<0, 4>([&]<int k>() { a2[4 * v + k][i] = x[k]; });
-                    });
-                });
-                fold(m[ch], l[ch], ac[ch], a.pre_ml[2 * row], a.pre_ml[2 * row + 1], a2);
-            }
-            write_final(row, ac[ch], l[ch]);
-        });
-    };
-
-    // Leaves the unit at `u` after sub-tile `g_last`.  A unit inside this
-    // wave's range is finished here.  A unit split between k waves leaves k
-    // records (one per wave, at slot wave + unit) that the reduce pass merges
-    // after this launch; the wave holding the unit's first sub-tile describes
-    // the unit for it (first slot, k, row, KV head, chunk).
+    // Leaves the unit at `u` after sub-tile `g_last`.
+    //  * multi mode: a unit inside this wave's range is finished here; a unit
+    //    split between k waves leaves k records (one per wave, at slot
+    //    wave + unit), and the wave holding its first sub-tile describes it
+    //    (first slot, k, row, KV head, chunk, ...) for the reduce pass;
+    //  * shared mode: every unit leaves records (a sequence's result needs its
+    //    prefix and its suffix part), and the wave holding the first
+    //    sub-tile describes each of the unit's columns for the reduce pass:
+    //    where its records start, how many, which column of the records, and
+    //    (suffix) whether a prefix part exists.
     auto finish_unit = [&](const MCursor &u, int g_last) {
         float m[CH], l[CH];
         static_for<0, CH>([&]<int ch>() {
@@ -533,15 +508,29 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         const int ub = ua + u.n;
         const int unit = unit_index(u);
         const bool whole = seg_first == ua && g_last + 1 == ub;
-        if (seg_first == ua && lane == 0) {
+        typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+        if (seg_first == ua) {
             const int k = whole ? 1 : wave_of(ub - 1) - wave + 1;
-            typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-            int32_t *d = a.unit_desc + kDescWords * (1 + (int64_t)unit);
-            *reinterpret_cast<i32x4 *>(d) = i32x4{wave + unit, k, u.row, (u.kvh << 16) | u.chunk};
-            *reinterpret_cast<i32x4 *>(d + 4) = i32x4{u.tseq, u.cols, u.lo, 0};
+            if (mode == kModeMulti) {
+                if (lane == 0) {
+                    int32_t *d = a.unit_desc + kDescWords * (1 + (int64_t)unit);
+                    *reinterpret_cast<i32x4 *>(d) = i32x4{wave + unit, k, u.row, (u.kvh << 16) | u.chunk};
+                    *reinterpret_cast<i32x4 *>(d + 4) = i32x4{u.tseq, u.cols, u.lo, 0};
+                }
+            } else if (rg == 0) {
+                int32_t *cd = a.col_desc + (u.kind == kRowPrefix ? (int64_t)kColDescWords * a.num_seqs * Hq : 0);
+                const int flags = u.kind == kRowSuffix && u.lo > 0 ? kHasPrefix : 0;
+                static_for<0, CH>([&]<int ch>() {
+                    if (orow[ch] >= 0)
+                        *reinterpret_cast<i32x4 *>(cd + kColDescWords * orow[ch]) =
+                            i32x4{wave + unit, k, ch * kMultiCols + c, flags};
+                });
+            }
         }
-        if (whole) {
-            finalize(u, m, l, acc);
+        if (whole && mode == kModeMulti) {
+            static_for<0, CH>([&]<int ch>() {
+                if (orow[ch] >= 0) write_final(orow[ch], acc[ch], l[ch]);
+            });
             return;
         }
         store_segment((int64_t)wave + unit, m, l, acc);
@@ -620,31 +609,110 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     }
 }
 
-// Merges the records of every unit the main pass split, and writes the
-// unit's result as the main pass would have.  One workgroup per unit at a
-// time; thread t owns column t % 16 of each chunk and dims
-// [(t / 16) * D / 16, (t / 16 + 1) * D / 16).  The (max, sum) pairs of up to
-// kReduceBatch records are loaded together, then their acc slices together,
-// and folded in record order.
+// The reduce pass.  Sixteen threads own one output row, each a slice of
+// D / 16 dims; a record is read at one column.  The (max, sum) pairs and the
+// acc slices of up to kReduceBatch records are loaded together and folded in
+// record order, so an output costs one or two round trips whatever the
+// number of records.
 constexpr int kReduceThreads = 256;
-constexpr int kMaxReduceGroups = 2048;
 constexpr int kReduceBatch = 16;
+constexpr int kMaxReduceGroups = 2048;
+
+template <int D, int UC>
+__device__ __forceinline__ void fold_records(const MultiArgs &a, int64_t base, int k, int col, int d0, float &m,
+                                             float &l, f32x4 (&acc)[D / 64]) {
+    constexpr int NV = D / 64;   // float4s per thread and record
+    constexpr int kRecFloats = UC * D;
+    // a descriptor left over from a description that broke its
+    // preconditions must not send the loads out of the record array
+    if (base < 0 || k < 0 || col < 0 || col >= UC || base + k > (int64_t)kMaxWaves + a.max_units) k = 0;
+    for (int r0 = 0; r0 < k; r0 += kReduceBatch) {
+        const int nb = min(kReduceBatch, k - r0);
+        float mb[kReduceBatch], lb[kReduceBatch];
+        f32x4 xb[kReduceBatch][NV];
+#pragma unroll
+        for (int b = 0; b < kReduceBatch; ++b) {
+            if (b < nb) {
+                const int64_t slot = base + r0 + b;
+                mb[b] = a.ws_ml[(slot * UC + col) * 2];
+                lb[b] = a.ws_ml[(slot * UC + col) * 2 + 1];
+                const f32x4 *src = reinterpret_cast<const f32x4 *>(a.ws_acc + slot * kRecFloats + col * D + d0);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) xb[b][v] = src[v];
+            }
+        }
+        float mn = m;
+#pragma unroll
+        for (int b = 0; b < kReduceBatch; ++b) mn = b < nb ? fmaxf(mn, mb[b]) : mn;
+        const float mu = mn == kNegInf ? 0.f : mn;
+        const float x = fast_exp2(m - mu);
+        l *= x;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] *= x;
+#pragma unroll
+        for (int b = 0; b < kReduceBatch; ++b) {
+            if (b < nb) {
+                const float w = fast_exp2(mb[b] - mu);
+                l = __builtin_fmaf(w, lb[b], l);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[v][e] = __builtin_fmaf(w, xb[b][v][e], acc[v][e]);
+                }
+            }
+        }
+        m = mn;
+    }
+}
+
+template <typename DT, int D>
+__device__ __forceinline__ void write_row(const MultiArgs &a, int64_t orow, int d0, float l, const f32x4 (&acc)[D / 64]) {
+    constexpr int NV = D / 64;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[4 * v + e] = acc[v][e] * inv;
+    }
+    const u32x4 pk = pack_chunk<DT>(f);
+    char *o = static_cast<char *>(a.out) + orow * (D * 2) + d0 * 2;
+    if constexpr (NV == 2) *reinterpret_cast<u32x4 *>(o) = pk;
+    else *reinterpret_cast<u32x2 *>(o) = u32x2{pk[0], pk[1]};
+}
 
 template <typename DT, int D, int CH>
 __global__ __launch_bounds__(kReduceThreads) void attn_multi_reduce(MultiArgs a) {
     constexpr int UC = kMultiCols * CH;
-    constexpr int kRecFloats = UC * D;
-    constexpr int DPT = D / 16;          // dims per thread (4 or 8)
-    constexpr int NV = DPT / 4;          // float4s per thread and record
+    constexpr int NV = D / 64;
+    constexpr int kRowsPerGroup = kReduceThreads / 16;
     const int t = threadIdx.x;
-    const int c = t & 15;
-    const int d0 = (t >> 4) * DPT;
-    const int units = a.unit_desc[0];
+    const int d0 = (t & 15) * (D / 16);
     typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    if (a.mode == kModeShared) {
+        // one output row per (sequence, q head): its suffix records, then its
+        // prefix records
+        const int64_t items = (int64_t)a.num_seqs * a.num_q_heads;
+        for (int64_t item = (int64_t)blockIdx.x * kRowsPerGroup + (t >> 4); item < items;
+             item += (int64_t)gridDim.x * kRowsPerGroup) {
+            const i32x4 sd = *reinterpret_cast<const i32x4 *>(a.col_desc + kColDescWords * item);
+            float m = kNegInf, l = 0.f;
+            f32x4 acc[NV];
+            for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+            fold_records<D, UC>(a, sd[0], sd[1], sd[2], d0, m, l, acc);
+            if (sd[3] & kHasPrefix) {
+                const i32x4 pd = *reinterpret_cast<const i32x4 *>(a.col_desc + kColDescWords * (items + item));
+                fold_records<D, UC>(a, pd[0], pd[1], pd[2], d0, m, l, acc);
+            }
+            write_row<DT, D>(a, item, d0, l, acc);
+        }
+        return;
+    }
+    // multi mode: the units the main pass split, one per group of 16 rows
+    const int units = a.unit_desc[0];
     for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int32_t *d = a.unit_desc + kDescWords * (1 + (int64_t)unit);
         const i32x4 dsc = *reinterpret_cast<const i32x4 *>(d);
-        const int64_t base = dsc[0];
         const int k = dsc[1];
         if (k <= 1) continue;
         const i32x4 dsc2 = *reinterpret_cast<const i32x4 *>(d + 4);
@@ -653,82 +721,15 @@ __global__ __launch_bounds__(kReduceThreads) void attn_multi_reduce(MultiArgs a)
         ri.tseq = dsc2[0];
         ri.cols = dsc2[1];
         ri.lo = dsc2[2];
-        for (int ch = 0; ch < CH; ++ch) {
-            const int col = ch * kMultiCols + c;
-            const int64_t orow = column_row(a, row, ri, kvh, (chunk * CH + ch) * kMultiCols + c);
+        ri.kind = kRowMulti;
+        for (int col = t >> 4; col < UC; col += kRowsPerGroup) {
+            const int64_t orow = column_row(a, row, ri, kvh, chunk * UC + col);
             if (orow < 0) continue;
             float m = kNegInf, l = 0.f;
             f32x4 acc[NV];
             for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int r0 = 0; r0 < k; r0 += kReduceBatch) {
-                const int nb = min(kReduceBatch, k - r0);
-                float mb[kReduceBatch], lb[kReduceBatch];
-                f32x4 xb[kReduceBatch][NV];
-#pragma unroll
-                for (int b = 0; b < kReduceBatch; ++b) {
-                    if (b < nb) {
-                        const int64_t slot = base + r0 + b;
-                        mb[b] = a.ws_ml[(slot * UC + col) * 2];
-                        lb[b] = a.ws_ml[(slot * UC + col) * 2 + 1];
-                        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.ws_acc + slot * kRecFloats + col * D + d0);
-#pragma unroll
-                        for (int v = 0; v < NV; ++v) xb[b][v] = src[v];
-                    }
-                }
-                float mn = m;
-#pragma unroll
-                for (int b = 0; b < kReduceBatch; ++b) mn = b < nb ? fmaxf(mn, mb[b]) : mn;
-                const float mu = mn == kNegInf ? 0.f : mn;
-                const float x = fast_exp2(m - mu);
-                l *= x;
-                for (int v = 0; v < NV; ++v) acc[v] *= x;
-#pragma unroll
-                for (int b = 0; b < kReduceBatch; ++b) {
-                    if (b < nb) {
-                        const float w = fast_exp2(mb[b] - mu);
-                        l = __builtin_fmaf(w, lb[b], l);
-#pragma unroll
-                        for (int v = 0; v < NV; ++v) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) acc[v][e] = __builtin_fmaf(w, xb[b][v][e], acc[v][e]);
-                        }
-                    }
-                }
-                m = mn;
-            }
-            if (a.mode == kModePrefix) {
-                f32x4 *dst = reinterpret_cast<f32x4 *>(a.pre_acc + orow * D + d0);
-                for (int v = 0; v < NV; ++v) dst[v] = acc[v];
-                if (t < 16) {
-                    a.pre_ml[2 * orow] = m;
-                    a.pre_ml[2 * orow + 1] = l;
-                }
-                continue;
-            }
-            if (a.mode == kModeSuffix && ri.lo > 0) {
-                const float m2 = a.pre_ml[2 * orow], l2 = a.pre_ml[2 * orow + 1];
-                const f32x4 *pa = reinterpret_cast<const f32x4 *>(a.pre_acc + orow * D + d0);
-                const float mn = fmaxf(m, m2);
-                const float mu = mn == kNegInf ? 0.f : mn;
-                const float x = fast_exp2(m - mu), y = fast_exp2(m2 - mu);
-                l = l * x + l2 * y;
-                for (int v = 0; v < NV; ++v) {
-                    const f32x4 p2 = pa[v];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[v][e] = __builtin_fmaf(p2[e], y, acc[v][e] * x);
-                }
-            }
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) f[4 * v + e] = acc[v][e] * inv;
-            }
-            const u32x4 pk = pack_chunk<DT>(f);
-            char *o = static_cast<char *>(a.out) + orow * (D * 2) + d0 * 2;
-            if constexpr (DPT == 8) *reinterpret_cast<u32x4 *>(o) = pk;
-            else *reinterpret_cast<u32x2 *>(o) = u32x2{pk[0], pk[1]};
+            fold_records<D, UC>(a, dsc[0], k, col, d0, m, l, acc);
+            write_row<DT, D>(a, orow, d0, l, acc);
         }
     }
 }
@@ -738,8 +739,10 @@ hipError_t launch_multi_typed(const MultiArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.num_waves / kWavesPerGroup));
     attn_multi_kernel<DT, D, CH><<<grid, dim3(kWavesPerGroup * kWave), 0, stream>>>(a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    // the reduce pass: enough workgroups to cover the split units quickly
-    const int groups = a.max_units < kMaxReduceGroups ? a.max_units : kMaxReduceGroups;
+    // the reduce pass: enough workgroups to cover the split units (multi) or
+    // the output rows (shared) in one round
+    int64_t groups = a.mode == kModeShared ? ((int64_t)a.num_seqs * a.num_q_heads + 15) / 16 : a.max_units;
+    groups = groups < kMaxReduceGroups ? groups : kMaxReduceGroups;
     attn_multi_reduce<DT, D, CH><<<dim3((unsigned)(groups > 0 ? groups : 1)), dim3(kReduceThreads), 0, stream>>>(a);
     return hipGetLastError();
 }

@@ -200,11 +200,12 @@ int64_t multi_units(int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_he
 }
 int64_t shared_units(int32_t num_seqs, int32_t num_groups, int32_t num_q_heads, int32_t num_kv_heads) {
     const int64_t G = num_q_heads / num_kv_heads;
-    // prefix rows: sum over groups of ceil(members * G / 16) <= ceil(S * G / 16) + groups
+    // prefix rows: sum over groups of ceil(members * G / 16) <= ceil(S * G / 16) + groups;
+    // suffix rows: ceil(G / 16) per (sequence, KV head); one launch holds both
     const int64_t pre = (int64_t)num_kv_heads * (((int64_t)num_seqs * G + pkv::kMultiCols - 1) / pkv::kMultiCols +
                                                  num_groups);
-    const int64_t suf = (int64_t)num_seqs * num_kv_heads;
-    return pre > suf ? pre : suf;
+    const int64_t suf = (int64_t)num_seqs * num_kv_heads * ((G + pkv::kMultiCols - 1) / pkv::kMultiCols);
+    return pre + suf;
 }
 
 int log2_exact(int32_t x) {
@@ -261,10 +262,9 @@ int multi_waves(int32_t dtype, int32_t head_dim, int32_t chunks, int64_t *waves)
 void fill_multi_split(pkv::MultiArgs &a, const pkv::MultiWorkspace &ws, void *workspace) {
     char *w = static_cast<char *>(workspace);
     a.unit_desc = reinterpret_cast<int32_t *>(w + ws.desc_offset);
+    a.col_desc = reinterpret_cast<int32_t *>(w + ws.col_desc_offset);
     a.ws_acc = reinterpret_cast<float *>(w + ws.acc_offset);
     a.ws_ml = reinterpret_cast<float *>(w + ws.ml_offset);
-    a.pre_acc = reinterpret_cast<float *>(w + ws.pre_acc_offset);
-    a.pre_ml = reinterpret_cast<float *>(w + ws.pre_ml_offset);
 }
 
 }  // namespace
@@ -356,11 +356,9 @@ int paged_attn_decode_shared(void *out, const void *q, const void *k_cache, cons
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
     // prefix rows have (members x group) columns: the mean group size decides
     const int64_t G = num_q_heads / num_kv_heads;
-    const int32_t pre_chunks = chunks_for(((int64_t)num_seqs * G + num_groups - 1) / num_groups);
-    const int32_t suf_chunks = chunks_for(G);
-    int64_t pre_waves = 0, suf_waves = 0;
-    if ((st = multi_waves(dtype, head_dim, pre_chunks, &pre_waves)) != PKV_OK) return st;
-    if ((st = multi_waves(dtype, head_dim, suf_chunks, &suf_waves)) != PKV_OK) return st;
+    const int32_t chunks = chunks_for(((int64_t)num_seqs * G + num_groups - 1) / num_groups);
+    int64_t waves = 0;
+    if ((st = multi_waves(dtype, head_dim, chunks, &waves)) != PKV_OK) return st;
     pkv::MultiArgs a{};
     a.out = out;
     a.q = q;
@@ -380,16 +378,13 @@ int paged_attn_decode_shared(void *out, const void *q, const void *k_cache, cons
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_context_len = max_context_len;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-    // the shared prefix of every group once for all its members, then each
-    // sequence's own suffix merged with its prefix record (stream order)
-    a.mode = pkv::kModePrefix;
-    a.num_rows = num_groups;
-    a.num_waves = (int32_t)pre_waves;
-    if (pkv::launch_attn_multi(dtype, head_dim, pre_chunks, a, stream) != hipSuccess) return PKV_ERR_HIP;
-    a.mode = pkv::kModeSuffix;
-    a.num_rows = num_seqs;
-    a.num_waves = (int32_t)suf_waves;
-    return pkv::launch_attn_multi(dtype, head_dim, suf_chunks, a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    // one pass streams every group's shared prefix once for all its members
+    // and every sequence's own suffix; the reduce pass merges the two parts
+    a.mode = pkv::kModeShared;
+    a.num_groups = num_groups;
+    a.num_rows = num_groups + num_seqs;
+    a.num_waves = (int32_t)waves;
+    return pkv::launch_attn_multi(dtype, head_dim, chunks, a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 int paged_attn_decode(void *out, const void *q, const void *k_cache, const void *v_cache,

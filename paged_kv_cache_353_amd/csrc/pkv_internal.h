@@ -116,16 +116,15 @@ hipError_t launch_attn_decode(int32_t dtype, int32_t head_dim, int32_t group,
                               const DecodeArgs &a, hipStream_t stream);
 
 // ------------------------------------------------ many query columns per KV head
-// One kernel serves three row kinds.  A row is a sequence or a group of
-// sequences; each of its (KV head, column chunk) units streams the row's
-// tokens once for up to kMultiCols query columns.
+// One kernel serves two call kinds.  A row is a sequence or a group of
+// sequences; each of its (KV head, column chunks) units streams the row's
+// tokens once for up to kMultiCols * kMultiChunksMax query columns.
 enum MultiMode : int32_t {
     kModeMulti = 0,   // rows = sequences; columns = (query token, head), causal among the new tokens
-    kModePrefix = 1,  // rows = groups; tokens [0, P) shared by every member; columns = (member, head);
-                      // writes one (max, exp-sum, acc) record per (sequence, q head)
-    kModeSuffix = 2,  // rows = sequences; tokens [P, L); columns = heads; folds in the record
+    kModeShared = 1,  // rows = the groups' shared prefixes [0, P), columns = (member, head), then the
+                      // sequences' suffixes [P, L), columns = heads; a reduce pass merges the two
 };
-constexpr int kMultiCols = 16;  // query columns per chunk (the MFMA's N)
+constexpr int kMultiCols = 16;      // query columns per chunk (the MFMA's N)
 constexpr int kMultiChunksMax = 2;  // column chunks a unit streams together (one K/V load)
 // Resident waves per SIMD the many-column grid is sized for.  With two, the
 // younger wave of each SIMD streams at about 60% of the older one's rate and
@@ -139,18 +138,19 @@ struct MultiArgs {
     const void *v_cache;
     const int32_t *block_tables;
     const int32_t *context_lens;
-    const int32_t *group_starts;  // shared modes: [num_groups + 1]
-    const int32_t *prefix_lens;   // shared modes: [num_seqs]
-    float *pre_acc;               // shared modes: [num_seqs * num_q_heads][head_dim]
-    float *pre_ml;                // shared modes: [num_seqs * num_q_heads][2]
-    int32_t *unit_desc;           // [0]: units of the call; then 8 int32 per unit (from word 8):
-                                  // first record slot, records, row, (KV head << 16) | chunk,
+    const int32_t *group_starts;  // shared mode: [num_groups + 1]
+    const int32_t *prefix_lens;   // shared mode: [num_seqs]
+    int32_t *unit_desc;           // multi mode: [0] units of the call; then 8 int32 per unit (from
+                                  // word 8): first record slot, records, row, (KV head << 16) | chunk,
                                   // table sequence, columns, first attended position, 0
+    int32_t *col_desc;            // shared mode: 4 int32 per (sequence, q head), suffix part then
+                                  // prefix part: first record slot, records, column, flags
     float *ws_acc;                // [kMaxWaves + units][columns of a unit][head_dim] partial records
     float *ws_ml;                 // [kMaxWaves + units][columns of a unit][2]
     int32_t mode;
-    int32_t num_rows;             // sequences, or groups in the prefix mode
+    int32_t num_rows;             // multi: sequences; shared: groups + sequences
     int32_t num_seqs;
+    int32_t num_groups;           // shared mode
     int32_t max_units;            // units the workspace holds
     int32_t num_query_tokens;     // multi mode (1 otherwise)
     int32_t num_q_heads;
@@ -166,25 +166,23 @@ struct MultiArgs {
 // single-query decode is left in place (and untouched), so one workspace can
 // serve both kinds of call.
 struct MultiWorkspace {
-    size_t desc_offset;      // unit descriptors
+    size_t desc_offset;      // unit descriptors (multi)
+    size_t col_desc_offset;  // column descriptors (shared)
     size_t acc_offset;       // partial records
     size_t ml_offset;
-    size_t pre_acc_offset;   // prefix records (shared modes)
-    size_t pre_ml_offset;
     size_t bytes;
 };
 
-inline MultiWorkspace multi_workspace(int64_t max_units, int64_t pre_records, int32_t head_dim) {
+inline MultiWorkspace multi_workspace(int64_t max_units, int64_t items, int32_t head_dim) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t slots = (size_t)kMaxWaves + (size_t)max_units;
     const size_t cols = (size_t)kMultiCols * kMultiChunksMax;   // a record holds every column of a unit
     MultiWorkspace w{};
     w.desc_offset = up(kCounterBytes);
-    w.acc_offset = w.desc_offset + up((8 + 8 * (size_t)max_units) * sizeof(int32_t));
+    w.col_desc_offset = w.desc_offset + up((8 + 8 * (size_t)max_units) * sizeof(int32_t));
+    w.acc_offset = w.col_desc_offset + up(2 * 4 * (size_t)items * sizeof(int32_t));
     w.ml_offset = w.acc_offset + up(slots * cols * (size_t)head_dim * sizeof(float));
-    w.pre_acc_offset = w.ml_offset + up(slots * cols * 2 * sizeof(float));
-    w.pre_ml_offset = w.pre_acc_offset + up((size_t)pre_records * (size_t)head_dim * sizeof(float));
-    w.bytes = w.pre_ml_offset + up((size_t)pre_records * 2 * sizeof(float));
+    w.bytes = w.ml_offset + up(slots * cols * 2 * sizeof(float));
     return w;
 }
 
