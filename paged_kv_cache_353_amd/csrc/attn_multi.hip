@@ -352,6 +352,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     int64_t orow[CH];        // multi/suffix: output row of the column; prefix: record index; -1 absent
     float m_run[CH], l_run[CH];   // reference and this lane's share of the exp-sum
     f32x4 acc[CH][DL];       // acc[ch][e][i]: dim (4rg + i) * DL + e
+    int nch = CH;            // chunks of the unit with at least one column (wave-uniform)
     int seg_first = g0;
 
     auto start_unit = [&](const MCursor &u) {
@@ -368,6 +369,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             qspan = Hq;
         }
         const RowInfo ri{u.t0, u.tend, u.lo, u.L, u.tseq, u.cols, u.kind};
+        nch = uniform(min(CH, (u.cols - u.chunk * CH * kMultiCols + kMultiCols - 1) / kMultiCols));
         const char *qb = static_cast<const char *>(a.q) + uniform(qbase * ROW);
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, uniform(qspan * ROW), kBufferFlags);
         static_for<0, CH>([&]<int ch>() {
@@ -399,6 +401,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         const int lo = u.lo;
         u32x2 ph[CH], pl[CH];
         static_for<0, CH>([&]<int ch>() {
+            if (ch > 0 && ch >= nch) return;   // a chunk with no column: no work
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
             static_for<0, NLK>([&]<int b>() { s = mfma_chunk<DT>(kr[b], qr[ch][b], s); });
             float sv[4];
@@ -434,9 +437,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         static_for<0, DL>([&]<int e>() {
             const u32x2 av = {v_half<e>(vr[0]) | (v_half<e>(vr[1]) << 16),
                               v_half<e>(vr[2]) | (v_half<e>(vr[3]) << 16)};
-            static_for<0, CH>([&]<int ch>() { acc[ch][e] = mfma_pv<DT>(av, ph[ch], acc[ch][e]); });
+            static_for<0, CH>([&]<int ch>() {
+                if (ch == 0 || ch < nch) acc[ch][e] = mfma_pv<DT>(av, ph[ch], acc[ch][e]);
+            });
             if constexpr (std::is_same_v<DT, BF16>) {
-                static_for<0, CH>([&]<int ch>() { acc[ch][e] = mfma_pv<DT>(av, pl[ch], acc[ch][e]); });
+                static_for<0, CH>([&]<int ch>() {
+                    if (ch == 0 || ch < nch) acc[ch][e] = mfma_pv<DT>(av, pl[ch], acc[ch][e]);
+                });
             }
         });
     };
