@@ -132,14 +132,25 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         }
     }
 
-    // ---- total work T (sub-tiles over all units) and this wave's range
+    // ---- total work T (sub-tiles over all units) and this wave's range.  A
+    // batch of at most 64 sequences is read and scanned once, and the scan is
+    // kept for locating the wave's start.
+    const bool one_batch = S <= kWave;
     int N = 0;
-    for (int base = 0; base < S; base += kWave) {
-        const int i = base + lane;
-        const int L = i < S ? tilesL(a.context_lens[i]) : 0;
-        N += (L + 15) >> 4;
+    int L0 = 0, n0 = 0, incl0 = 0;
+    if (one_batch) {
+        L0 = lane < S ? tilesL(a.context_lens[lane]) : 0;
+        n0 = (L0 + 15) >> 4;
+        incl0 = wave_incl_scan(n0, lane);
+        N = uniform(__builtin_amdgcn_readlane(incl0, kWave - 1));
+    } else {
+        for (int base = 0; base < S; base += kWave) {
+            const int i = base + lane;
+            const int L = i < S ? tilesL(a.context_lens[i]) : 0;
+            N += (L + 15) >> 4;
+        }
+        N = uniform(wave_sum_i(N, lane));
     }
-    N = uniform(wave_sum_i(N, lane));
     // sub-tile indices fit in 32 bits (the host rejects larger batches);
     // products with a wave count are formed in 64 bits
     const int T = N * Hkv;
@@ -174,7 +185,17 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
 
     // ---- locate g0: sequence (prefix scan of sub-tile counts), KV head, sub-tile
     Cursor cur{};
-    {
+    if (one_batch) {
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(incl0 * Hkv > g0);   // g0 < T: never empty
+        const int f = __builtin_ctzll(hit);
+        cur.seq = f;
+        cur.L = __builtin_amdgcn_readlane(L0, f);
+        cur.n = __builtin_amdgcn_readlane(n0, f);
+        cur.pre = __builtin_amdgcn_readlane(incl0 - n0, f);
+        const int rem = g0 - cur.pre * Hkv;
+        cur.kvh = rem / cur.n;
+        cur.sub = rem - cur.kvh * cur.n;
+    } else {
         int pre = 0;
         for (int base = 0; base < S; base += kWave) {
             const int i = base + lane;

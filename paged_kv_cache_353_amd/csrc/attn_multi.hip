@@ -224,21 +224,50 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         }
     }
 
-    // ---- total work and this wave's range (equal contiguous shares)
+    // ---- total work and this wave's range (equal contiguous shares).  Up to
+    // kCachedBatches batches of 64 rows are read and scanned once, and the
+    // scans are kept for locating the wave's start; longer calls read the
+    // rows a second time.
+    constexpr int kCachedBatches = 4;
+    const bool cached = R <= kCachedBatches * kWave;
+    int tlc[kCachedBatches], unc[kCachedBatches], inc[kCachedBatches], uinc[kCachedBatches];
     int N = 0, U = 0;
-    for (int base = 0; base < R; base += kWave) {
-        const int r = base + lane;
-        if (r < R) {
-            const RowInfo ri = row_info(r, ld_vec);
-            const int n = tiles_of(ri);
-            N += Hkv * chunks_of(ri) * n;
-            U += n > 0 ? Hkv * chunks_of(ri) : 0;
+    if (cached) {
+        int carry = 0, ucarry = 0;
+        static_for<0, kCachedBatches>([&]<int b>() {
+            tlc[b] = 0;
+            unc[b] = 0;
+            const int r = b * kWave + lane;
+            if (r < R) {
+                const RowInfo ri = row_info(r, ld_vec);
+                const int n = tiles_of(ri);
+                unc[b] = n > 0 ? Hkv * chunks_of(ri) : 0;
+                tlc[b] = unc[b] * n;
+            }
+            inc[b] = carry + wave_incl_scan(tlc[b], lane);
+            uinc[b] = ucarry + wave_incl_scan(unc[b], lane);
+            carry = __builtin_amdgcn_readlane(inc[b], kWave - 1);
+            ucarry = __builtin_amdgcn_readlane(uinc[b], kWave - 1);
+        });
+        N = carry;
+        U = ucarry;
+    } else {
+        for (int base = 0; base < R; base += kWave) {
+            const int r = base + lane;
+            if (r < R) {
+                const RowInfo ri = row_info(r, ld_vec);
+                const int n = tiles_of(ri);
+                N += Hkv * chunks_of(ri) * n;
+                U += n > 0 ? Hkv * chunks_of(ri) : 0;
+            }
         }
+        N = wave_sum_i(N, lane);
+        U = wave_sum_i(U, lane);
     }
-    const int T = uniform(wave_sum_i(N, lane));
+    const int T = uniform(N);
     // a group description that breaks its preconditions (overlapping groups)
     // could ask for more units than the workspace holds: do nothing then
-    const int units = uniform(wave_sum_i(U, lane));
+    const int units = uniform(U);
     const bool too_many = units > a.max_units;
     if (wave == 0 && lane == 0) a.unit_desc[0] = too_many ? 0 : units;   // units the reduce pass visits
     if (too_many) return;
@@ -265,7 +294,20 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
 
     // ---- locate g0: row (prefix scans of sub-tiles and units), then unit and sub-tile
     MCursor cur{};
-    {
+    if (cached) {
+        bool found = false;
+        static_for<0, kCachedBatches>([&]<int b>() {
+            if (found) return;
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(inc[b] > g0);
+            if (hit) {
+                const int f = __builtin_ctzll(hit);
+                cur.row = b * kWave + f;
+                cur.pre = __builtin_amdgcn_readlane(inc[b] - tlc[b], f);
+                cur.upre = __builtin_amdgcn_readlane(uinc[b] - unc[b], f);
+                found = true;
+            }
+        });
+    } else {
         int pre = 0, upre = 0;
         for (int base = 0; base < R; base += kWave) {
             const int r = base + lane;
@@ -289,6 +331,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             pre += __builtin_amdgcn_readlane(incl, kWave - 1);
             upre += __builtin_amdgcn_readlane(uincl, kWave - 1);
         }
+    }
+    {
         cur.row = uniform(cur.row);
         cur.pre = uniform(cur.pre);
         cur.upre = uniform(cur.upre);

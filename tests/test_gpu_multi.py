@@ -119,3 +119,15 @@ def test_multi_wide_score_range(gain):
     inp = W.build_decode_inputs([5, 64, 700, 3000], 32, 8, 128, 16, "bf16", 300, seed=83, device=DEV)
     q4 = (W.multi_query(inp, 3, seed=84).float() * gain).to(torch.bfloat16)
     check_multi(inp, q4, what=f"multi gain {gain}")
+
+
+def test_multi_many_sequences():
+    """More rows than the kernel's prologue keeps in registers (256)."""
+    say("case: multi, 300 sequences, T=2")
+    lens = np.random.default_rng(85).integers(1, 400, size=300)
+    inp = W.build_decode_inputs(lens, 8, 2, 64, 16, "f16", int(sum(-(-lens // 16))) + 8, seed=86, device=DEV)
+    q4 = W.multi_query(inp, 2, seed=87)
+    rng = np.random.default_rng(88)
+    triples = [(int(i), int(j), int(h)) for i, j, h in zip(rng.integers(0, 300, 200), rng.integers(0, 2, 200),
+                                                           rng.integers(0, 8, 200))]
+    check_multi(inp, q4, triples=triples, what="multi 300 seqs")

@@ -163,3 +163,14 @@ def test_shared_workspace_reuse_and_matches_plain_decode():
                                     inp.block_size, inp.scale, inp.dtype)
     assert_close(o1, want, "bf16", what="shared reuse")
     assert_close(ref, want, "bf16", what="plain decode")
+
+
+def test_shared_many_groups():
+    """More rows (groups + sequences) than the prologue keeps in registers."""
+    say("case: shared, 90 prompts x 3 forks (360 rows)")
+    inp = _forked([40 + 3 * k for k in range(90)], 3, 5, 8, 2, 64, 16, "bf16", seed=97)
+    h = host_inputs(inp)
+    gs, pl = shared_prefix_groups(h["block_tables"], h["context_lens"], inp.block_size)
+    rng = np.random.default_rng(98)
+    pairs = [(int(i), int(hh)) for i, hh in zip(rng.integers(0, len(pl), 200), rng.integers(0, 8, 200))]
+    check_shared(inp, gs, pl, pairs=pairs, what="shared many groups")
