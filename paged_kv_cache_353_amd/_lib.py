@@ -105,6 +105,30 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+class _on_device:
+    """Makes ``device`` current for the duration of a call (the library
+    launches on the current HIP device), skipping the switch when it already
+    is: the context manager costs several microseconds per call."""
+
+    __slots__ = ("index", "prev")
+
+    def __init__(self, device: torch.device):
+        self.index = device.index if device.index is not None else torch.cuda.current_device()
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if cur != self.index:
+            self.prev = cur
+            torch.cuda.set_device(self.index)
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+        return False
+
+
 def paged_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
                    v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
     """Scatter new tokens' K/V ([num_tokens, num_kv_heads, head_dim]) into the
@@ -125,7 +149,7 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
         raise ValueError("caches and slot_mapping must be contiguous")
     nb, hkv, bs, d = k_cache.shape
     lib = load_library()
-    with torch.cuda.device(k_cache.device):
+    with _on_device(k_cache.device):
         _check(lib.paged_kv_write(
             k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             slot_mapping.data_ptr(), k.shape[0], hkv, d, bs, nb, k.stride(0), v.stride(0),
@@ -144,7 +168,7 @@ def paged_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
         raise ValueError("caches and block_pairs must be contiguous")
     nb, hkv, bs, d = k_cache.shape
     lib = load_library()
-    with torch.cuda.device(k_cache.device):
+    with _on_device(k_cache.device):
         _check(lib.paged_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_pairs.data_ptr(),
                                      block_pairs.shape[0], hkv, d, bs, nb, _dtype_code(k_cache),
                                      _stream_handle(k_cache.device)))
@@ -200,7 +224,7 @@ def paged_decode_step(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v
     need = int(lib.paged_attn_decode_workspace_size(S, hq, hkv, d, bs, int(max_context_len)))
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         _check(lib.paged_decode_step(
             out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
             v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, hq, hkv, d,
@@ -240,7 +264,7 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     need = int(lib.paged_attn_decode_workspace_size(S, hq, hkv, d, bs, int(max_context_len)))
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         _check(lib.paged_attn_decode(
             out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), context_lens.data_ptr(), S, hq, hkv, d, bs, mb, nb,
@@ -297,7 +321,7 @@ def paged_attn_decode_multi(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     need = int(lib.paged_attn_decode_multi_workspace_size(S, T, hq, hkv, d))
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         _check(lib.paged_attn_decode_multi(
             out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), context_lens.data_ptr(), S, T, hq, hkv, d, bs, mb, nb,
@@ -345,7 +369,7 @@ def paged_attn_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.
     need = int(lib.paged_attn_decode_shared_workspace_size(S, ng, hq, hkv, d))
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         _check(lib.paged_attn_decode_shared(
             out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), context_lens.data_ptr(), group_starts.data_ptr(),
