@@ -215,10 +215,10 @@ int paged_decode_step(void *out, const void *q, const void *k_new, const void *v
  *
  *   out, q        [num_seqs, num_query_tokens, num_q_heads, head_dim], 16-byte
  *                 aligned, dtype of the caches
- *   dtype         PKV_F16 or PKV_BF16 (PKV_F32: PKV_ERR_UNSUPPORTED); products
- *                 run on matrix cores with fp32 accumulation; the softmax
- *                 weights multiply V as fp16 (11 significant bits) or as a
- *                 bf16 head plus a bf16 remainder (about 16 bits)
+ *   dtype         PKV_F32, PKV_F16 or PKV_BF16; products run on matrix cores
+ *                 with fp32 accumulation; the softmax weights multiply V as
+ *                 fp32, as fp16 (11 significant bits) or as a bf16 head plus a
+ *                 bf16 remainder (about 16 bits)
  *   head_dim      64 or 128; block_size a power of two from 16 to 256; any
  *                 num_q_heads / num_kv_heads
  *   workspace     >= paged_attn_decode_multi_workspace_size(...) bytes,

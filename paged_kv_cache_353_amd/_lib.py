@@ -305,7 +305,7 @@ def paged_attn_decode_multi(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
     """Several query tokens per sequence: ``q``/``out`` are
     [num_seqs, num_query_tokens, num_q_heads, head_dim]; query token ``j`` of
     sequence ``i`` sits at position ``L_i - T + j`` (already in the cache) and
-    attends to ``[0, L_i - T + j + 1)``.  fp16/bf16 only.  Other arguments and
+    attends to ``[0, L_i - T + j + 1)``.  Other arguments and
     the workspace contract as for ``paged_attn_decode``.  Returns ``out``."""
     if q.dim() != 4 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must both be [num_seqs, num_query_tokens, num_q_heads, head_dim]")
@@ -351,7 +351,7 @@ def paged_attn_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.
     ``group_starts[g] .. group_starts[g+1] - 1``, and their tables share the
     blocks of the first ``prefix_lens[i]`` positions (see
     ``sharing.shared_prefix_groups``).  The result equals ``paged_attn_decode``.
-    fp16/bf16 only.  Returns ``out``."""
+    Returns ``out``."""
     _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, block_size)
     S, hq, d = q.shape
     if group_starts.dtype != torch.int32 or prefix_lens.dtype != torch.int32:

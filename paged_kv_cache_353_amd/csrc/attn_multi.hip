@@ -112,10 +112,16 @@ __device__ __forceinline__ void split_probs_bf16(const float (&p)[4], u32x2 &hi,
     lo = u32x2{cvt2_bf16(r[0], r[1]), cvt2_bf16(r[2], r[3])};
 }
 
-// 16-bit element E of a lane's slice of a V row (dword E/2, half E%2).
-template <int E, typename VR>
-__device__ __forceinline__ uint32_t v_half(const VR &v) {
-    const uint32_t w = v[E / 2];
+// A lane's slice of one V row: D / 16 consecutive elements, as 32-bit words.
+template <int VW>
+struct VRow {
+    uint32_t w[VW];
+};
+
+// 16-bit element E of a lane's slice of a V row (word E/2, half E%2).
+template <int E, int VW>
+__device__ __forceinline__ uint32_t v_half(const VRow<VW> &v) {
+    const uint32_t w = v.w[E / 2];
     return (E & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
@@ -179,14 +185,15 @@ __device__ __forceinline__ int64_t column_row(const MultiArgs &a, int row, const
 template <typename DT, int D, int CH>
 __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(MultiArgs a) {
     constexpr int EB = DT::kBytes;
-    static_assert(EB == 2, "16-bit caches only");
+    constexpr bool kF32 = EB == 4;
     constexpr int ROW = D * EB;      // bytes per token row
-    constexpr int NLK = D / 32;      // 16-byte K loads per lane per sub-tile (one per 32-dim MFMA step)
-    constexpr int DL = D / 16;       // dims of a V row per lane (and 16x16x16 MFMAs per sub-tile)
+    constexpr int NLK = ROW / 64;    // 16-byte K loads per lane per sub-tile
+    constexpr int DL = D / 16;       // dims of a V row per lane (and output slices per sub-tile)
     constexpr int DQ = D / 4;        // output dims owned by a lane
+    constexpr int VW = DL * EB / 4;  // 32-bit words of a lane's slice of a V row (2, 4 or 8)
     constexpr int UC = kMultiCols * CH;   // query columns of a unit
     constexpr int kRecFloats = UC * D;    // floats of a record's acc
-    typedef typename std::conditional<DL == 8, u32x4, u32x2>::type VReg;
+    typedef VRow<VW> VReg;
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
     static_assert(CH >= 1 && CH <= kMultiChunksMax, "column chunks per unit");
 
@@ -365,7 +372,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     const int BS = 1 << a.block_shift;
     const int64_t head_bytes = (int64_t)BS * ROW;
     const int64_t block_bytes = (int64_t)Hkv * head_bytes;
-    const int koff = c * ROW + 16 * rg;              // K: token c, dims 32b + 8rg ..
+    const int koff = c * ROW + 16 * rg;              // K: token c, bytes 64b + 16rg ..
     const int voff = 4 * rg * ROW + c * DL * EB;     // V: tokens 4rg + m, dims c*DL ..
 
     auto issue = [&](const MCursor &u, bool live, u32x4 (&kr)[NLK], VReg (&vr)[4]) {
@@ -383,8 +390,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vc + off), 0, nbytes, kBufferFlags);
         static_for<0, NLK>([&]<int b>() { kr[b] = load_chunk(rk, koff + 64 * b); });
         static_for<0, 4>([&]<int m>() {
-            if constexpr (DL == 8) vr[m] = load_chunk(rv, voff + m * ROW);
-            else vr[m] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + m * ROW, 0, 0));
+            if constexpr (VW == 2) {
+                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + m * ROW, 0, 0));
+                vr[m].w[0] = x[0];
+                vr[m].w[1] = x[1];
+            } else {
+                static_for<0, VW / 4>([&]<int h>() {
+                    const u32x4 x = load_chunk(rv, voff + m * ROW + 16 * h);
+                    static_for<0, 4>([&]<int k>() { vr[m].w[4 * h + k] = x[k]; });
+                });
+            }
         });
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -444,6 +459,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         const int tok = u.t0 + (u.sub << 4) + 4 * rg;
         const int lo = u.lo;
         u32x2 ph[CH], pl[CH];
+        float pf[CH][4];   // fp32: the probabilities themselves
         static_for<0, CH>([&]<int ch>() {
             if (ch > 0 && ch >= nch) return;   // a chunk with no column: no work
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -476,20 +492,35 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             static_for<0, 4>([&]<int r>() { p[r] = fast_exp2(sv[r] - mu); });
             l_run[ch] += (p[0] + p[1]) + (p[2] + p[3]);
             if constexpr (std::is_same_v<DT, BF16>) split_probs_bf16(p, ph[ch], pl[ch]);
-            else ph[ch] = pack_probs_f16(p);
+            else if constexpr (std::is_same_v<DT, F16>) ph[ch] = pack_probs_f16(p);
+            else static_for<0, 4>([&]<int r>() { pf[ch][r] = p[r]; });
         });
-        static_for<0, DL>([&]<int e>() {
-            const u32x2 av = {v_half<e>(vr[0]) | (v_half<e>(vr[1]) << 16),
-                              v_half<e>(vr[2]) | (v_half<e>(vr[3]) << 16)};
-            static_for<0, CH>([&]<int ch>() {
-                if (ch == 0 || ch < nch) acc[ch][e] = mfma_pv<DT>(av, ph[ch], acc[ch][e]);
-            });
-            if constexpr (std::is_same_v<DT, BF16>) {
-                static_for<0, CH>([&]<int ch>() {
-                    if (ch == 0 || ch < nch) acc[ch][e] = mfma_pv<DT>(av, pl[ch], acc[ch][e]);
+        if constexpr (kF32) {
+            // 16x16x4 fp32 MFMA, step r over tokens {4k + r}: the B operand of
+            // lane (k, j) is its own probability r, the A operand V row 4k + r
+            static_for<0, DL>([&]<int e>() {
+                static_for<0, 4>([&]<int r>() {
+                    const float av = as_f(vr[r].w[e]);
+                    static_for<0, CH>([&]<int ch>() {
+                        if (ch == 0 || ch < nch)
+                            acc[ch][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, pf[ch][r], acc[ch][e], 0, 0, 0);
+                    });
                 });
-            }
-        });
+            });
+        } else {
+            static_for<0, DL>([&]<int e>() {
+                const u32x2 av = {v_half<e>(vr[0]) | (v_half<e>(vr[1]) << 16),
+                                  v_half<e>(vr[2]) | (v_half<e>(vr[3]) << 16)};
+                static_for<0, CH>([&]<int ch>() {
+                    if (ch == 0 || ch < nch) acc[ch][e] = mfma_pv<DT>(av, ph[ch], acc[ch][e]);
+                });
+                if constexpr (std::is_same_v<DT, BF16>) {
+                    static_for<0, CH>([&]<int ch>() {
+                        if (ch == 0 || ch < nch) acc[ch][e] = mfma_pv<DT>(av, pl[ch], acc[ch][e]);
+                    });
+                }
+            });
+        }
     };
 
     // ---- results.  A lane's dims in record / output order: (i, e) -> i * DL + e.
@@ -502,11 +533,18 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         const float inv = l > 0.f ? 1.f / l : 0.f;
         char *o = static_cast<char *>(a.out) + row * ROW + rg * DQ * EB;
         static_for<0, 4>([&]<int i>() {
-            float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            static_for<0, DL>([&]<int e>() { f[e] = ac[e][i] * inv; });
-            const u32x4 pk = pack_chunk<DT>(f);
-            if constexpr (DL == 8) *reinterpret_cast<u32x4 *>(o + i * 16) = pk;
-            else *reinterpret_cast<u32x2 *>(o + i * 8) = u32x2{pk[0], pk[1]};
+            if constexpr (kF32) {
+                static_for<0, DL / 4>([&]<int h>() {
+                    *reinterpret_cast<f32x4 *>(o + (i * DL + 4 * h) * 4) =
+                        f32x4{ac[4 * h][i] * inv, ac[4 * h + 1][i] * inv, ac[4 * h + 2][i] * inv, ac[4 * h + 3][i] * inv};
+                });
+            } else {
+                float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                static_for<0, DL>([&]<int e>() { f[e] = ac[e][i] * inv; });
+                const u32x4 pk = pack_chunk<DT>(f);
+                if constexpr (DL == 8) *reinterpret_cast<u32x4 *>(o + i * 16) = pk;
+                else *reinterpret_cast<u32x2 *>(o + i * 8) = u32x2{pk[0], pk[1]};
+            }
         });
     };
     // Stores a (max, exp-sum, acc) record of one column: acc at racc + col * D,
@@ -726,10 +764,17 @@ __device__ __forceinline__ void write_row(const MultiArgs &a, int64_t orow, int 
 #pragma unroll
         for (int e = 0; e < 4; ++e) f[4 * v + e] = acc[v][e] * inv;
     }
-    const u32x4 pk = pack_chunk<DT>(f);
-    char *o = static_cast<char *>(a.out) + orow * (D * 2) + d0 * 2;
-    if constexpr (NV == 2) *reinterpret_cast<u32x4 *>(o) = pk;
-    else *reinterpret_cast<u32x2 *>(o) = u32x2{pk[0], pk[1]};
+    constexpr int EB = DT::kBytes;
+    char *o = static_cast<char *>(a.out) + orow * (D * EB) + d0 * EB;
+    if constexpr (EB == 4) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            *reinterpret_cast<f32x4 *>(o + 16 * v) = f32x4{f[4 * v], f[4 * v + 1], f[4 * v + 2], f[4 * v + 3]};
+    } else {
+        const u32x4 pk = pack_chunk<DT>(f);
+        if constexpr (NV == 2) *reinterpret_cast<u32x4 *>(o) = pk;
+        else *reinterpret_cast<u32x2 *>(o) = u32x2{pk[0], pk[1]};
+    }
 }
 
 template <typename DT, int D, int CH>
@@ -819,16 +864,17 @@ int multi_waves_chunks(int chunks) {
 }  // namespace
 
 bool multi_supported(int32_t dtype, int32_t head_dim) {
-    return (dtype == 1 || dtype == 2) && (head_dim == 64 || head_dim == 128);
+    return (dtype == 0 || dtype == 1 || dtype == 2) && (head_dim == 64 || head_dim == 128);
 }
 
 int multi_waves_per_cu(int32_t dtype, int32_t head_dim, int32_t chunks) {
-    static std::atomic<int> cache[2][2][kMultiChunksMax];
+    static std::atomic<int> cache[3][2][kMultiChunksMax];
     if (!multi_supported(dtype, head_dim) || chunks < 1 || chunks > kMultiChunksMax) return 0;
-    const int di = dtype - 1, hi = head_dim == 128 ? 1 : 0;
+    const int di = dtype, hi = head_dim == 128 ? 1 : 0;
     int v = cache[di][hi][chunks - 1].load(std::memory_order_relaxed);
     if (v > 0) return v;
-    if (dtype == 1) v = head_dim == 128 ? multi_waves_chunks<F16, 128>(chunks) : multi_waves_chunks<F16, 64>(chunks);
+    if (dtype == 0) v = head_dim == 128 ? multi_waves_chunks<F32, 128>(chunks) : multi_waves_chunks<F32, 64>(chunks);
+    else if (dtype == 1) v = head_dim == 128 ? multi_waves_chunks<F16, 128>(chunks) : multi_waves_chunks<F16, 64>(chunks);
     else v = head_dim == 128 ? multi_waves_chunks<BF16, 128>(chunks) : multi_waves_chunks<BF16, 64>(chunks);
     if (v > 0) cache[di][hi][chunks - 1].store(v, std::memory_order_relaxed);
     return v;
@@ -836,6 +882,10 @@ int multi_waves_per_cu(int32_t dtype, int32_t head_dim, int32_t chunks) {
 
 hipError_t launch_attn_multi(int32_t dtype, int32_t head_dim, int32_t chunks, const MultiArgs &a,
                              hipStream_t stream) {
+    if (dtype == 0) {
+        return head_dim == 128 ? launch_multi_chunks<F32, 128>(chunks, a, stream)
+                               : launch_multi_chunks<F32, 64>(chunks, a, stream);
+    }
     if (dtype == 1) {
         return head_dim == 128 ? launch_multi_chunks<F16, 128>(chunks, a, stream)
                                : launch_multi_chunks<F16, 64>(chunks, a, stream);

@@ -204,7 +204,7 @@ def test_multi_and_shared_reject_bad_arguments_on_host(lib):
                                             a["maxL"], a["scale"], a["dtype"], a["ws"], a["wsb"], None)
 
     for f in (multi, shared):
-        assert f(dtype=0) == PKV_ERR_UNSUPPORTED          # fp32 caches: single-query kernels only
+        assert f(dtype=0) == PKV_ERR_WORKSPACE            # fp32 caches are accepted
         assert f(dtype=7) == PKV_ERR_DTYPE
         assert f(D=96) == PKV_ERR_UNSUPPORTED
         assert f(bs=48, mb=8) == PKV_ERR_UNSUPPORTED      # not a power of two

@@ -37,7 +37,7 @@ def check_multi(inp, q4, triples=None, what=""):
                              pairs=pairs, what=what)
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv,T", [(8, 8, 1), (8, 2, 1), (8, 2, 3), (16, 2, 2), (4, 2, 8),
                                       (2, 2, 16), (8, 2, 5), (16, 1, 2), (6, 2, 7), (8, 2, 16)])
@@ -47,6 +47,15 @@ def test_multi_small_shapes(dtype, D, Hq, Hkv, T):
     inp = W.build_decode_inputs(lens, Hq, Hkv, D, 16, dtype, 200, seed=71 + T, device=DEV)
     q4 = W.multi_query(inp, T, seed=72 + T)
     check_multi(inp, q4, what=f"multi {dtype} D={D} G={Hq // Hkv} T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 4, 9])
+def test_multi_fp32_long_split(T):
+    say(f"case: multi fp32, 2 sequences of 9000 / 300 tokens, T={T}")
+    inp = W.build_decode_inputs([9000, 300], 32, 8, 128, 16, "f32", 620, seed=89 + T, device=DEV)
+    q4 = W.multi_query(inp, T, seed=90 + T)
+    triples = [(0, 0, 0), (0, T - 1, 31), (0, T // 2, 7), (1, 0, 5), (1, T - 1, 26)]
+    check_multi(inp, q4, triples=triples, what=f"multi fp32 long T={T}")
 
 
 @pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])

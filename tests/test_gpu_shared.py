@@ -114,7 +114,7 @@ def test_shared_prefix_copy_on_write_variant():
     check_shared(inp, gs, pl, pairs=pairs, what="shared prefix 1000")
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv,samples", [(8, 8, 3), (8, 2, 4), (32, 8, 8), (16, 2, 5), (2, 2, 20)])
 def test_shared_small_shapes(dtype, D, Hq, Hkv, samples):
