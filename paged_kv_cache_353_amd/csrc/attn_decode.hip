@@ -690,6 +690,25 @@ hipError_t launch_group(int group, const DecodeArgs &a, hipStream_t s) {
     }
 }
 
+template <typename DT, int D, int G>
+int scratch_typed() {
+    hipFuncAttributes attr{};
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(attn_stream_kernel<DT, D, G>)) != hipSuccess)
+        return 0;
+    return (int)attr.localSizeBytes;
+}
+
+template <typename DT, int D>
+int scratch_group(int group) {
+    switch (group) {
+        case 1: return scratch_typed<DT, D, 1>();
+        case 2: return scratch_typed<DT, D, 2>();
+        case 4: return scratch_typed<DT, D, 4>();
+        case 8: return scratch_typed<DT, D, 8>();
+        default: return 0;
+    }
+}
+
 template <typename DT, int D>
 int waves_group(int group) {
     switch (group) {
@@ -745,6 +764,24 @@ int decode_waves_per_cu(int32_t dtype, int32_t head_dim, int32_t group) {
     }
     if (v > 0) cache[dtype][hd][gi].store(v, std::memory_order_relaxed);
     return v;
+}
+
+int decode_scratch_bytes(int32_t dtype, int32_t head_dim, int32_t group) {
+    // a property of the compiled kernel: asked once per configuration
+    static std::atomic<int> cache[3][2][4];
+    if (!decode_supported(dtype, head_dim, group)) return 0;
+    const int hd = head_dim == 128 ? 1 : 0;
+    const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
+    int v = cache[dtype][hd][gi].load(std::memory_order_relaxed);
+    if (v != 0) return v > 0 ? v : 0;
+    int b = 0;
+    switch (dtype) {
+        case 0: b = head_dim == 128 ? scratch_group<F32, 128>(group) : scratch_group<F32, 64>(group); break;
+        case 1: b = head_dim == 128 ? scratch_group<F16, 128>(group) : scratch_group<F16, 64>(group); break;
+        default: b = head_dim == 128 ? scratch_group<BF16, 128>(group) : scratch_group<BF16, 64>(group); break;
+    }
+    cache[dtype][hd][gi].store(b > 0 ? b : -1, std::memory_order_relaxed);
+    return b;
 }
 
 hipError_t launch_attn_decode(int32_t dtype, int32_t head_dim, int32_t group,

@@ -59,7 +59,39 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
     }
 }
 
+// Append at the end of each context: the token of sequence i goes to
+// position L_i - 1 (L_i = context_lens[i], clamped to max_context_len), whose
+// slot comes from the sequence's Block Table.  One workgroup per sequence;
+// sequences with L_i == 0 write nothing.
+__global__ __launch_bounds__(256) void append_last_kernel(AppendLastArgs a) {
+    const int i = blockIdx.x;
+    int L = a.context_lens[i];
+    L = L < a.max_context_len ? L : a.max_context_len;
+    if (L <= 0) return;
+    const int pos = L - 1;
+    const int j = pos / a.block_size;
+    const int64_t phys = a.block_tables[(int64_t)i * a.max_blocks_per_seq + j];
+    const int64_t row_bytes = (int64_t)a.head_dim * a.elem_bytes;
+    const int chunks = (int)(row_bytes / 16);
+    for (int idx = threadIdx.x; idx < a.num_kv_heads * chunks; idx += blockDim.x) {
+        const int h = idx / chunks, c = idx - h * chunks;
+        const int64_t src = ((int64_t)i * a.num_kv_heads + h) * row_bytes + (int64_t)c * 16;
+        const int64_t dst = ((phys * a.num_kv_heads + h) * a.block_size + (pos - j * a.block_size)) * row_bytes +
+                            (int64_t)c * 16;
+        const u32x4 kx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.k_new) + src);
+        const u32x4 vx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.v_new) + src);
+        *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_cache) + dst) = kx;
+        *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_cache) + dst) = vx;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_append_last(const AppendLastArgs &a, hipStream_t stream) {
+    if (a.num_seqs == 0) return hipSuccess;
+    append_last_kernel<<<dim3((unsigned)a.num_seqs), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+}
 
 hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t stream) {
     if (a.num_pairs == 0) return hipSuccess;

@@ -107,12 +107,30 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
         block_size <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads != 0 ||
         (int64_t)num_seqs * num_kv_heads > pkv::kMaxUnits)
         return 0;
-    return pkv::decode_workspace(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim).bytes;
+    const int32_t group = num_q_heads / num_kv_heads;
+    const size_t one = pkv::decode_workspace(num_seqs, num_kv_heads, group, head_dim).bytes;
+    // enough for the many-column kernel too, which serves the group sizes the
+    // one-query kernel does not (or would only serve with register spills)
+    const int64_t units = (int64_t)num_seqs * num_kv_heads * ((group + pkv::kMultiCols - 1) / pkv::kMultiCols);
+    if (units > pkv::kMaxUnits) return one;
+    const size_t many = pkv::multi_workspace(units, 0, head_dim).bytes;
+    return one > many ? one : many;
 }
 
 }  // extern "C"
 
 namespace {
+
+// One query per sequence through the many-column kernel (T = 1), after the
+// appended tokens are written (fused step); defined with the other
+// many-column entry points below.
+int decode_through_multi(void *out, const void *q, const void *k_new, const void *v_new,
+                         const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                         const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                         float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 // Shared by paged_attn_decode (k_new == v_new == NULL) and paged_decode_step.
 int decode_impl(void *out, const void *q, const void *k_new, const void *v_new,
@@ -132,8 +150,18 @@ int decode_impl(void *out, const void *q, const void *k_new, const void *v_new,
     if ((int64_t)num_seqs * num_kv_heads > pkv::kMaxUnits) return PKV_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
     const int32_t group = num_q_heads / num_kv_heads;
-    if (!pkv::decode_supported(dtype, head_dim, group)) return PKV_ERR_UNSUPPORTED;
-    if (block_size % 16 != 0 || block_size > 256) return PKV_ERR_UNSUPPORTED;
+    // The one-query kernel serves group sizes 1, 2, 4 and 8 where it keeps
+    // its state in registers; other group sizes, and configurations whose
+    // compiled kernel spills (head_dim 128 with 8 query heads per KV head:
+    // about ten times slower), go to the many-column kernel.
+    const bool one_query = pkv::decode_supported(dtype, head_dim, group) && block_size % 16 == 0 &&
+                           block_size <= 256 &&
+                           !(num_seqs > 0 && pkv::decode_scratch_bytes(dtype, head_dim, group) > 0);
+    if (!one_query)
+        return decode_through_multi(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    max_blocks_per_seq, num_blocks, max_context_len, scale, dtype, workspace,
+                                    workspace_bytes, stream);
     // sub-tile indices of the whole batch are kept in 32 bits
     if ((int64_t)num_seqs * num_kv_heads * (((int64_t)max_context_len + 15) / 16) >= ((int64_t)1 << 31))
         return PKV_ERR_UNSUPPORTED;
@@ -265,6 +293,67 @@ void fill_multi_split(pkv::MultiArgs &a, const pkv::MultiWorkspace &ws, void *wo
     a.col_desc = reinterpret_cast<int32_t *>(w + ws.col_desc_offset);
     a.ws_acc = reinterpret_cast<float *>(w + ws.acc_offset);
     a.ws_ml = reinterpret_cast<float *>(w + ws.ml_offset);
+}
+
+int decode_through_multi(void *out, const void *q, const void *k_new, const void *v_new,
+                         const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                         const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                         float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    const int64_t units = multi_units(num_seqs, 1, num_q_heads, num_kv_heads);
+    int st = multi_checks(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                          num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                          scale, dtype, units);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    if ((k_new == nullptr) != (v_new == nullptr)) return PKV_ERR_NULL;
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGN;
+    const pkv::MultiWorkspace ws = pkv::multi_workspace(units, 0, head_dim);
+    if (!workspace || workspace_bytes < ws.bytes) return PKV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
+    const int32_t chunks = chunks_for(num_q_heads / num_kv_heads);
+    int64_t waves = 0;
+    if ((st = multi_waves(dtype, head_dim, chunks, &waves)) != PKV_OK) return st;
+    if (k_new) {
+        // the appended token of each sequence first, at position L - 1
+        pkv::AppendLastArgs ap{};
+        ap.k_new = k_new;
+        ap.v_new = v_new;
+        ap.k_cache = const_cast<void *>(k_cache);
+        ap.v_cache = const_cast<void *>(v_cache);
+        ap.block_tables = block_tables;
+        ap.context_lens = context_lens;
+        ap.num_seqs = num_seqs;
+        ap.num_kv_heads = num_kv_heads;
+        ap.head_dim = head_dim;
+        ap.block_size = block_size;
+        ap.max_blocks_per_seq = max_blocks_per_seq;
+        ap.max_context_len = max_context_len;
+        ap.elem_bytes = elem_bytes(dtype);
+        if (pkv::launch_append_last(ap, stream) != hipSuccess) return PKV_ERR_HIP;
+    }
+    pkv::MultiArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    fill_multi_split(a, ws, workspace);
+    a.mode = pkv::kModeMulti;
+    a.num_rows = num_seqs;
+    a.num_seqs = num_seqs;
+    a.max_units = (int32_t)units;
+    a.num_query_tokens = 1;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_shift = log2_exact(block_size);
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.num_waves = (int32_t)waves;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    return pkv::launch_attn_multi(dtype, head_dim, chunks, a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 }  // namespace

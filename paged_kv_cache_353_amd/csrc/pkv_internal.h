@@ -36,6 +36,27 @@ struct CopyBlocksArgs {
 
 hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t stream);
 
+// ---------------------------------------------------------------- append at L - 1
+// The token of each sequence written to position context_len - 1 (the slot
+// looked up in the Block Table); used ahead of a decode that cannot append.
+struct AppendLastArgs {
+    const void *k_new;            // [num_seqs][num_kv_heads][head_dim]
+    const void *v_new;
+    void *k_cache;
+    void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    int32_t num_seqs;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;
+    int32_t elem_bytes;
+};
+
+hipError_t launch_append_last(const AppendLastArgs &a, hipStream_t stream);
+
 // ---------------------------------------------------------------- decode
 constexpr int kWavesPerGroup = 4;   // independent waves per workgroup
 constexpr int kWavesPerSimd = 2;    // resident waves per SIMD the grid is sized for (at most)
@@ -107,6 +128,11 @@ inline DecodeWorkspace decode_workspace(int32_t num_seqs, int32_t num_kv_heads, 
 }
 
 bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group);
+
+// Bytes of per-lane scratch (register spills) of the one-query kernel for this
+// configuration; a configuration that spills is routed to the many-column
+// kernel instead (0 on error).
+int decode_scratch_bytes(int32_t dtype, int32_t head_dim, int32_t group);
 
 // Resident waves per CU of the decode kernel for this configuration (0 on error).
 int decode_waves_per_cu(int32_t dtype, int32_t head_dim, int32_t group);

@@ -74,7 +74,9 @@ def test_workspace_size_rules(lib):
     assert w % 256 == 0
     assert f(64, 32, 8, 128, 16, 256) == w            # independent of the context length
     assert f(4, 32, 8, 128, 16, 1 << 20) > 0
-    assert f(8, 8, 8, 64, 16, 100) < f(8, 64, 8, 64, 16, 100)   # grows with the group
+    assert f(8, 8, 8, 64, 16, 100) <= f(8, 64, 8, 64, 16, 100)  # does not shrink with the group
+    # enough for the many-column kernel, which serves other group sizes
+    assert f(8, 24, 8, 64, 16, 100) == pkv.paged_attn_decode_multi_workspace_size(8, 1, 24, 8, 64)
     assert f(-1, 32, 8, 128, 16, 100) == 0
     assert f(0, 32, 8, 128, 16, 100) == 0
     assert f(4, 30, 8, 128, 16, 100) == 0             # heads not a multiple
@@ -97,7 +99,7 @@ def test_decode_rejects_bad_arguments_on_host(lib):
     assert _decode(lib, out=None) == PKV_ERR_NULL
     assert _decode(lib, dtype=7) == PKV_ERR_DTYPE
     assert _decode(lib, D=96) == PKV_ERR_UNSUPPORTED
-    assert _decode(lib, Hq=24, Hkv=8) == PKV_ERR_UNSUPPORTED     # group 3
+    assert _decode(lib, Hq=24, Hkv=8) == PKV_ERR_WORKSPACE       # group 3: the many-column kernel
     assert _decode(lib, Hq=30, Hkv=8) == PKV_ERR_SHAPE           # not a multiple
     assert _decode(lib, bs=8, mb=32) == PKV_ERR_UNSUPPORTED
     assert _decode(lib, bs=24, mb=16) == PKV_ERR_UNSUPPORTED

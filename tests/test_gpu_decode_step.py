@@ -119,3 +119,23 @@ def test_fused_step_long_context_sampled():
     say(f"  worst normwise error {worst:.2e}")
     del inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(24, 8), (12, 2), (32, 2), (16, 1), (64, 8)])
+def test_other_group_sizes_step_and_decode(dtype, Hq, Hkv):
+    """Group sizes the one-query kernel does not hold in registers (3, 6, 16,
+    and 8 at head_dim 128) go through the many-column kernel, with the append
+    written first in a fused step."""
+    say(f"case: group size {Hq // Hkv} dtype={dtype} (step, then decode)")
+    lens = [1, 2, 17, 300, 1500]
+    inp = W.build_decode_inputs(lens, Hq, Hkv, 128, 16, dtype, 200, seed=120 + Hq, device=DEV)
+    check_step(inp, dtype, what=f"step G={Hq // Hkv} {dtype}")
+    out = torch.empty_like(inp.q)
+    pkv.paged_attn_decode(out, inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.context_lens,
+                          inp.block_size, inp.scale, max_context_len=inp.max_context_len)
+    torch.cuda.synchronize()
+    h = host_inputs(inp)
+    want = oracle.paged_attn_decode(h["q"], h["k_cache"], h["v_cache"], h["block_tables"], h["context_lens"],
+                                    inp.block_size, inp.scale, dtype)
+    assert_close(out, want, dtype, what=f"decode G={Hq // Hkv} {dtype}")
