@@ -249,6 +249,19 @@ def main() -> int:
         o, s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens, s.block_size, s.scale,
         max_context_len=maxL, workspace=workspace), K)
 
+    # per-call durations of the step on the rotating copies (an event pair
+    # around every call), for the spread: p10 / median / p90
+    n_each = min(K, 100)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_each)]
+    for k in range(n_each):
+        ev[k][0].record(stream)
+        step(sets[k % nsets], outs[k % nsets])
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    each = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    pick = lambda f: round(each[min(len(each) - 1, int(f * (len(each) - 1) + 0.5))], 3)
+    step_spread = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "calls": n_each}
+
     # warm (single set, back to back) step time, for context
     warm = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     warm[0].record(stream)
@@ -349,6 +362,7 @@ def main() -> int:
         "separate_write_then_decode_us": round(separate_us, 3),
         "decode_only_us": round(decode_only_us, 3),
         "warm_step_us": round(warm_us, 3),
+        "step_us_per_call": step_spread,
         "wall_s": round(wall, 4),
         "roofline": {"bound": "hbm", "kernel": "attn_stream_kernel (paged_decode_step: append + decode, one launch)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
