@@ -28,9 +28,10 @@
  *
  * Errors: every call returns a pkv_status_t.  Arguments are checked on the host
  * only (no device reads, no synchronisation); a failed check returns before
- * anything is launched.  Preconditions on device-resident data are NOT checked:
- * block ids used by a sequence lie in [0, num_blocks); non-negative slots are
- * distinct and below num_blocks*block_size; 0 <= context_lens[i] <= max_context_len.
+ * anything is launched.  Preconditions on device-resident data are NOT checked
+ * by the compute calls (paged_check_inputs checks them on request): block ids
+ * used by a sequence lie in [0, num_blocks); non-negative slots are distinct
+ * and below num_blocks*block_size; 0 <= context_lens[i] <= max_context_len.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -275,6 +276,31 @@ int paged_attn_decode_shared(void *out, const void *q, const void *k_cache, cons
                              int32_t max_blocks_per_seq, int64_t num_blocks,
                              int32_t max_context_len, float scale, int32_t dtype,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_check_inputs -- check the device-resident data the other calls take on
+ * trust (a debugging aid; it reads only the arguments named here).
+ *
+ * Violations looked for (kinds):
+ *   1  context_lens[i] outside [0, max_context_len]
+ *   2  a Block Table entry a sequence uses (j < ceil(L_i / block_size)) outside
+ *      [0, num_blocks); padding entries past that are never read and not checked
+ *   3  a non-negative slot_mapping entry at or past num_blocks * block_size
+ *   4  a non-negative slot given twice (only with a bitmap)
+ *   slot_mapping  int64 [num_tokens] on the device, or NULL with num_tokens 0
+ *   bitmap        device scratch of ceil(num_blocks*block_size / 32) uint32
+ *                 (cleared by the call), or NULL to skip the repeat check
+ *   result        int64 [4] on the device, written in stream order: the
+ *                 number of violations, then the kind, index (sequence or
+ *                 token) and value of one of them (kind 0 and index -1 if none)
+ * Errors: PKV_ERR_SHAPE / PKV_ERR_NULL / PKV_ERR_ALIGN (pointers not aligned to
+ * their element) / PKV_ERR_WORKSPACE (bitmap too small) on the host, as for the
+ * other calls.  Nothing is synchronised.
+ */
+int paged_check_inputs(const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+                       int32_t max_blocks_per_seq, int64_t num_blocks, int32_t block_size,
+                       int32_t max_context_len, const int64_t *slot_mapping, int64_t num_tokens,
+                       uint32_t *bitmap, size_t bitmap_bytes, int64_t *result, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -84,6 +84,9 @@ def load_library() -> ctypes.CDLL:
                                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i64,
                                                  c_i32, c_f, c_i32, c_p, c_sz, c_p]
         lib.paged_attn_decode_shared.restype = c_int
+        lib.paged_check_inputs.argtypes = [c_p, c_p, c_i32, c_i32, c_i64, c_i32, c_i32, c_p, c_i64,
+                                           c_p, c_sz, c_p, c_p]
+        lib.paged_check_inputs.restype = c_int
         _lib = lib
         return lib
 
@@ -172,6 +175,44 @@ def paged_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
         _check(lib.paged_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_pairs.data_ptr(),
                                      block_pairs.shape[0], hkv, d, bs, nb, _dtype_code(k_cache),
                                      _stream_handle(k_cache.device)))
+
+
+CHECK_KINDS = {1: "context length out of range", 2: "block id out of range",
+               3: "slot out of range", 4: "slot given twice"}
+
+
+def paged_check_inputs(block_tables: torch.Tensor, context_lens: torch.Tensor, num_blocks: int,
+                       block_size: int, max_context_len: int,
+                       slot_mapping: Optional[torch.Tensor] = None,
+                       check_repeats: bool = True) -> torch.Tensor:
+    """Check on the device the data the compute calls take on trust.  Returns
+    int64 [4] on the tables' device: (violations, kind, index, value), kind 0 and
+    index -1 when there is none.  Nothing is synchronised."""
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or context_lens.shape != (block_tables.shape[0],):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
+    if not (block_tables.is_contiguous() and context_lens.is_contiguous()):
+        raise ValueError("block_tables and context_lens must be contiguous")
+    dev = block_tables.device
+    ntok, sptr = 0, None
+    if slot_mapping is not None:
+        if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or not slot_mapping.is_contiguous():
+            raise ValueError("slot_mapping must be contiguous int64 [num_tokens]")
+        ntok, sptr = slot_mapping.shape[0], (slot_mapping.data_ptr() if slot_mapping.numel() else None)
+    result = torch.empty(4, dtype=torch.int64, device=dev)
+    bitmap, bptr, bbytes = None, None, 0
+    if check_repeats and ntok > 0:
+        words = (int(num_blocks) * int(block_size) + 31) // 32
+        bitmap = torch.empty(max(words, 1), dtype=torch.int32, device=dev)
+        bptr, bbytes = bitmap.data_ptr(), bitmap.numel() * 4
+    lib = load_library()
+    with _on_device(dev):
+        _check(lib.paged_check_inputs(block_tables.data_ptr(), context_lens.data_ptr(),
+                                      block_tables.shape[0], block_tables.shape[1], int(num_blocks),
+                                      int(block_size), int(max_context_len), sptr, ntok, bptr, bbytes,
+                                      result.data_ptr(), _stream_handle(dev)))
+    return result
 
 
 def paged_attn_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,

@@ -85,7 +85,74 @@ __global__ __launch_bounds__(256) void append_last_kernel(AppendLastArgs a) {
     }
 }
 
+// Input checks (a debugging aid): the device-resident data the decode and
+// append calls take on trust.  One thread per sequence checks its length and
+// the table entries it uses; one thread per token checks its slot, and marks
+// it in a bitmap to find repeats.  Every violation is counted; one of them is
+// described.
+__device__ void report(int64_t *result, int kind, int64_t index, int64_t value) {
+    auto *r = reinterpret_cast<unsigned long long *>(result);
+    atomicAdd(r, 1ull);
+    if (atomicCAS(r + 1, 0ull, (unsigned long long)kind) == 0ull) {
+        result[2] = index;
+        result[3] = value;
+    }
+}
+
+__global__ __launch_bounds__(256) void check_init_kernel(CheckArgs a) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx == 0) {
+        a.result[0] = 0;
+        a.result[1] = 0;
+        a.result[2] = -1;
+        a.result[3] = 0;
+    }
+    for (int64_t w = idx; w < a.bitmap_words; w += (int64_t)gridDim.x * blockDim.x) a.bitmap[w] = 0u;
+}
+
+__global__ __launch_bounds__(256) void check_kernel(CheckArgs a) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx < a.num_seqs) {
+        const int L = a.context_lens[idx];
+        if (L < 0 || L > a.max_context_len) {
+            report(a.result, 1, idx, L);
+        } else {
+            const int n = (L + a.block_size - 1) / a.block_size;
+            for (int j = 0; j < n; ++j) {
+                const int32_t b = a.block_tables[idx * a.max_blocks_per_seq + j];
+                if (b < 0 || b >= a.num_blocks) {
+                    report(a.result, 2, idx, b);
+                    break;
+                }
+            }
+        }
+    }
+    if (a.slot_mapping != nullptr && idx < a.num_tokens) {
+        const int64_t s = a.slot_mapping[idx];
+        if (s >= 0) {
+            if (s >= a.num_blocks * (int64_t)a.block_size) {
+                report(a.result, 3, idx, s);
+            } else if (a.bitmap != nullptr) {
+                const uint32_t bit = 1u << (s & 31);
+                if (atomicOr(a.bitmap + (s >> 5), bit) & bit) report(a.result, 4, idx, s);
+            }
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_check(const CheckArgs &a, hipStream_t stream) {
+    const int64_t words = a.bitmap ? a.bitmap_words : 0;
+    int64_t init_groups = (words + 255) / 256;
+    init_groups = init_groups < 1 ? 1 : (init_groups > 4096 ? 4096 : init_groups);
+    check_init_kernel<<<dim3((unsigned)init_groups), dim3(256), 0, stream>>>(a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    const int64_t n = a.num_seqs > a.num_tokens ? a.num_seqs : a.num_tokens;
+    const int64_t groups = n > 0 ? (n + 255) / 256 : 1;
+    check_kernel<<<dim3((unsigned)groups), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+}
 
 hipError_t launch_append_last(const AppendLastArgs &a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;

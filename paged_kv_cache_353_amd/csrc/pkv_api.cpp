@@ -100,6 +100,39 @@ int paged_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_pairs,
     return pkv::launch_copy_blocks(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int paged_check_inputs(const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+                       int32_t max_blocks_per_seq, int64_t num_blocks, int32_t block_size,
+                       int32_t max_context_len, const int64_t *slot_mapping, int64_t num_tokens,
+                       uint32_t *bitmap, size_t bitmap_bytes, int64_t *result, hipStream_t stream) {
+    if (num_seqs < 0 || num_tokens < 0 || num_blocks <= 0 || block_size <= 0 || max_context_len < 0 ||
+        (num_seqs > 0 && max_blocks_per_seq <= 0))
+        return PKV_ERR_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size < max_context_len) return PKV_ERR_SHAPE;
+    if (!result) return PKV_ERR_NULL;
+    if (num_seqs > 0 && (!block_tables || !context_lens)) return PKV_ERR_NULL;
+    if (num_tokens > 0 && !slot_mapping) return PKV_ERR_NULL;
+    auto misaligned = [](const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; };
+    if (misaligned(result, 8) || misaligned(slot_mapping, 8) || misaligned(bitmap, 4) ||
+        misaligned(block_tables, 4) || misaligned(context_lens, 4))
+        return PKV_ERR_ALIGN;
+    const int64_t slots = num_blocks * (int64_t)block_size;
+    if (bitmap && bitmap_bytes < (size_t)((slots + 31) / 32) * 4) return PKV_ERR_WORKSPACE;
+    pkv::CheckArgs a{};
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.slot_mapping = num_tokens > 0 ? slot_mapping : nullptr;
+    a.bitmap = bitmap;
+    a.bitmap_words = bitmap ? (slots + 31) / 32 : 0;
+    a.result = result;
+    a.num_tokens = num_tokens;
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_seqs;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.block_size = block_size;
+    a.max_context_len = max_context_len;
+    return pkv::launch_check(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t block_size, int32_t max_context_len) {

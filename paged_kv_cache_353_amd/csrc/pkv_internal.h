@@ -57,6 +57,24 @@ struct AppendLastArgs {
 
 hipError_t launch_append_last(const AppendLastArgs &a, hipStream_t stream);
 
+// ---------------------------------------------------------------- input checks
+struct CheckArgs {
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    const int64_t *slot_mapping;   // may be null
+    uint32_t *bitmap;              // one bit per slot, may be null (no repeat check)
+    int64_t *result;               // [4]: violations, kind, index, value
+    int64_t bitmap_words;
+    int64_t num_tokens;
+    int64_t num_blocks;
+    int32_t num_seqs;
+    int32_t max_blocks_per_seq;
+    int32_t block_size;
+    int32_t max_context_len;
+};
+
+hipError_t launch_check(const CheckArgs &a, hipStream_t stream);
+
 // ---------------------------------------------------------------- decode
 constexpr int kWavesPerGroup = 4;   // independent waves per workgroup
 constexpr int kWavesPerSimd = 2;    // resident waves per SIMD the grid is sized for (at most)

@@ -44,7 +44,8 @@ def test_header_counter_region_constant():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("paged_kv_write", "paged_attn_decode", "paged_attn_decode_workspace_size",
-              "paged_decode_step", "paged_copy_blocks", "pkv_status_string", "pkv_version"):
+              "paged_decode_step", "paged_copy_blocks", "paged_attn_decode_multi",
+              "paged_attn_decode_shared", "paged_check_inputs", "pkv_status_string", "pkv_version"):
         assert n in names
 
 
@@ -230,3 +231,21 @@ def test_multi_and_shared_reject_bad_arguments_on_host(lib):
     assert pkv.paged_attn_decode_shared_workspace_size(4, 2, 32, 8, 128) > 0
     assert pkv.paged_attn_decode_shared_workspace_size(4, 5, 32, 8, 128) == 0
     assert multi(ws=(1 << 12) + 16, wsb=ws) == PKV_ERR_ALIGN
+
+
+def test_check_inputs_rejects_bad_arguments_on_host(lib):
+    def chk(**kw):
+        a = dict(bt=1 << 12, cl=1 << 12, S=4, mb=16, nb=64, bs=16, maxL=256, sm=1 << 12, n=8,
+                 bm=1 << 12, bmb=128, res=1 << 12)
+        a.update(kw)
+        return lib.paged_check_inputs(a["bt"], a["cl"], a["S"], a["mb"], a["nb"], a["bs"], a["maxL"], a["sm"],
+                                      a["n"], a["bm"], a["bmb"], a["res"], None)
+    assert chk(res=None) == PKV_ERR_NULL
+    assert chk(bt=None) == PKV_ERR_NULL
+    assert chk(sm=None) == PKV_ERR_NULL
+    assert chk(S=-1) == PKV_ERR_SHAPE
+    assert chk(nb=0) == PKV_ERR_SHAPE
+    assert chk(mb=8) == PKV_ERR_SHAPE                    # table too short for max_context_len
+    assert chk(res=(1 << 12) + 4) == PKV_ERR_ALIGN
+    assert chk(sm=(1 << 12) + 4) == PKV_ERR_ALIGN
+    assert chk(bmb=124) == PKV_ERR_WORKSPACE             # 64 * 16 slots need 32 words
