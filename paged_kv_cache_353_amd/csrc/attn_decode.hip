@@ -13,10 +13,11 @@
 //
 // Work split (one launch).  A unit is one (sequence, KV head) pair; its work
 // is ceil(L/16) sub-tiles of 16 tokens.  All sub-tiles of all units, in
-// (sequence, KV head, position) order, are cut into W equal contiguous ranges,
-// one per wave, W being what the GPU holds at once.  Every wave therefore
-// streams the same number of bytes whatever the length mix, with no empty
-// workgroups and no tail of short partitions.  A unit that lies wholly inside
+// (sequence, KV head, position) order, are cut into W contiguous ranges, one
+// per wave, W being what the GPU holds at once.  The cut is even once every
+// unit is charged a few sub-tiles more for the fixed cost of starting and
+// finishing it, so every wave takes about the same time whatever the length
+// mix, with no empty workgroups and no tail of short partitions.  A unit that lies wholly inside
 // one wave's range is finished by that wave; a unit shared by k waves gets k
 // partial results (max, exp-sum, un-normalised output) in the workspace, and
 // the wave that arrives last at the unit's counter merges them in a fixed
@@ -52,8 +53,10 @@ namespace {
 
 constexpr int kDirectMerge = 8;  // units split in at most this many pieces merge in one level
 constexpr int kDepth = 2;        // sub-tiles in flight per wave
-constexpr int kWeightOld = 1;    // relative share of the first half of the grid ...
-constexpr int kWeightYoung = 1;  // ... and of the second half
+// Fixed cost of a segment (loading q, the lane reductions, the partial record
+// and its arrival), in sub-tiles of streaming.  The split charges it to the
+// wave whose range holds the start of a unit.
+constexpr int kUnitCost = 4;
 
 // Position of a wave's load or compute stage in the (sequence, KV head,
 // sub-tile) order.  Every field is wave-uniform.
@@ -64,6 +67,7 @@ struct Cursor {
     int n;     // sub-tiles of the unit
     int L;     // tokens of the sequence read from the cache
     int pre;   // sub-tiles of one KV head summed over the sequences before `seq`
+    int cnt;   // sequences before `seq` with at least one sub-tile
 };
 
 // ------------------------------------------------------------------ the kernel
@@ -132,97 +136,114 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         }
     }
 
-    // ---- total work T (sub-tiles over all units) and this wave's range.  A
-    // batch of at most 64 sequences is read and scanned once, and the scan is
-    // kept for locating the wave's start.
+    // ---- total work and this wave's range.  Sub-tiles are ordered (sequence,
+    // KV head, position); a unit is a (sequence, KV head) pair with n >= 1 of
+    // them.  In a second, augmented order every unit is preceded by C ghost
+    // positions that stand for the fixed cost of a segment.  The augmented
+    // order is cut into equal ranges, and a wave processes the real sub-tiles
+    // of its range: a wave whose range holds unit starts streams fewer of
+    // them.  A batch of at most 64 sequences is read and scanned once, and the
+    // scan is kept for locating the range.
     const bool one_batch = S <= kWave;
-    int N = 0;
-    int L0 = 0, n0 = 0, incl0 = 0;
+    int N = 0, NU = 0;   // sub-tiles of one KV head, and sequences with any
+    int L0 = 0, n0 = 0, incl0 = 0, cinc0 = 0;
     if (one_batch) {
         L0 = lane < S ? tilesL(a.context_lens[lane]) : 0;
         n0 = (L0 + 15) >> 4;
         incl0 = wave_incl_scan(n0, lane);
+        cinc0 = wave_incl_scan(n0 > 0 ? 1 : 0, lane);
         N = uniform(__builtin_amdgcn_readlane(incl0, kWave - 1));
+        NU = uniform(__builtin_amdgcn_readlane(cinc0, kWave - 1));
     } else {
         for (int base = 0; base < S; base += kWave) {
             const int i = base + lane;
             const int L = i < S ? tilesL(a.context_lens[i]) : 0;
             N += (L + 15) >> 4;
+            NU += L > 0 ? 1 : 0;
         }
         N = uniform(wave_sum_i(N, lane));
+        NU = uniform(wave_sum_i(NU, lane));
     }
     // sub-tile indices fit in 32 bits (the host rejects larger batches);
-    // products with a wave count are formed in 64 bits
+    // augmented positions and products with a wave count take 64 bits
     const int T = N * Hkv;
-    const int Weff = T < W ? T : W;    // every wave below Weff gets >= 1 sub-tile
+    // Ghosts are used only when every range is longer than C, so that no
+    // range holds ghosts alone: then every wave gets at least one sub-tile.
+    int C = kUnitCost;
+    if (((int64_t)T + (int64_t)C * NU * Hkv) / W < C + 1) C = 0;
+    const int64_t TA = (int64_t)T + (int64_t)C * NU * Hkv;   // augmented length
+    const int Weff = C > 0 ? W : (T < W ? T : W);             // every wave below Weff gets >= 1 sub-tile
     if (wave >= Weff) return;
-    // Range boundaries: wave w starts at T * cum(w) / cum(Weff), where the
-    // first half of the grid (dispatched first, so older on every SIMD and
-    // favoured by the issue arbiter) may weigh kWeightOld against kWeightYoung
-    // for the second half.  Weights apply only when every range stays
-    // non-empty (at least two sub-tiles per wave); the split depends only on
-    // T and W, so results stay deterministic.
-    const bool weighted = kWeightOld != kWeightYoung && Weff == W && T >= 2 * W;
-    const int wa = weighted ? kWeightOld : 1;
-    const int wb = weighted ? kWeightYoung : 1;
-    const int half = Weff / 2;
-    auto cum = [&](int w) -> int64_t {
-        return (int64_t)wa * min(w, half) + (int64_t)wb * max(w - half, 0);
+    const int64_t x0 = TA * wave / Weff;                      // this wave's augmented range
+    const int64_t x1 = TA * (wave + 1) / Weff;
+    // the wave whose range holds augmented position x: the largest w with
+    // TA * w / Weff <= x
+    auto wave_of = [&](int64_t x) -> int {
+        const int64_t w = ((x + 1) * Weff - 1) / TA;
+        return (int)(w < Weff - 1 ? w : Weff - 1);
     };
-    const int64_t cum_all = cum(Weff);
-    auto start_of = [&](int w) -> int { return (int)((int64_t)T * cum(w) / cum_all); };
-    // the wave whose range holds sub-tile x: the largest w with start_of(w) <= x
-    auto wave_of = [&](int x) -> int {
-        const int64_t t = (int64_t)x * cum_all / T;
-        int w = t <= (int64_t)wa * half ? (int)(t / wa) : half + (int)((t - (int64_t)wa * half) / wb);
-        w = min(max(w, 0), Weff - 1);
-        while (w + 1 < Weff && start_of(w + 1) <= x) ++w;
-        while (w > 0 && start_of(w) > x) --w;
-        return w;
-    };
-    const int g0 = start_of(wave);
-    const int g1 = start_of(wave + 1);
 
-    // ---- locate g0: sequence (prefix scan of sub-tile counts), KV head, sub-tile
-    Cursor cur{};
+    // ---- locate the range's ends: the sequence (prefix scan of the augmented
+    // sub-tile counts), KV head and sub-tile of the first real sub-tile at or
+    // after x0, and the index of the first one at or after x1 (T past the end)
+    Cursor cur{}, endc{};
+    const bool has_end = x1 < TA;
+    auto pick = [&](Cursor &u, int f, int seq0, int pre, int cnt, int L, int n, int incl, int cinc) {
+        u.seq = seq0 + f;
+        u.L = __builtin_amdgcn_readlane(L, f);
+        u.n = __builtin_amdgcn_readlane(n, f);
+        u.pre = pre + __builtin_amdgcn_readlane(incl - n, f);
+        u.cnt = cnt + __builtin_amdgcn_readlane(cinc - (n > 0 ? 1 : 0), f);
+    };
     if (one_batch) {
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(incl0 * Hkv > g0);   // g0 < T: never empty
-        const int f = __builtin_ctzll(hit);
-        cur.seq = f;
-        cur.L = __builtin_amdgcn_readlane(L0, f);
-        cur.n = __builtin_amdgcn_readlane(n0, f);
-        cur.pre = __builtin_amdgcn_readlane(incl0 - n0, f);
-        const int rem = g0 - cur.pre * Hkv;
-        cur.kvh = rem / cur.n;
-        cur.sub = rem - cur.kvh * cur.n;
+        const int64_t ainc = (int64_t)(incl0 + C * cinc0) * Hkv;
+        pick(cur, __builtin_ctzll(__builtin_amdgcn_ballot_w64(ainc > x0)), 0, 0, 0, L0, n0, incl0, cinc0);
+        if (has_end)
+            pick(endc, __builtin_ctzll(__builtin_amdgcn_ballot_w64(ainc > x1)), 0, 0, 0, L0, n0, incl0, cinc0);
     } else {
-        int pre = 0;
+        int pre = 0, cnt = 0;
+        bool found0 = false;
         for (int base = 0; base < S; base += kWave) {
             const int i = base + lane;
             const int L = i < S ? tilesL(a.context_lens[i]) : 0;
             const int n = (L + 15) >> 4;
             const int incl = wave_incl_scan(n, lane);
-            const uint64_t hit = __builtin_amdgcn_ballot_w64((pre + incl) * Hkv > g0);
-            if (hit) {
-                const int f = __builtin_ctzll(hit);
-                cur.seq = base + f;
-                cur.L = __builtin_amdgcn_readlane(L, f);
-                cur.n = __builtin_amdgcn_readlane(n, f);
-                cur.pre = pre + __builtin_amdgcn_readlane(incl - n, f);
-                break;
+            const int cinc = wave_incl_scan(n > 0 ? 1 : 0, lane);
+            const int64_t ainc = ((int64_t)(pre + incl) + (int64_t)C * (cnt + cinc)) * Hkv;
+            const uint64_t hit0 = __builtin_amdgcn_ballot_w64(ainc > x0);
+            if (!found0 && hit0) {
+                pick(cur, __builtin_ctzll(hit0), base, pre, cnt, L, n, incl, cinc);
+                found0 = true;
+            }
+            if (found0) {
+                const uint64_t hit1 = __builtin_amdgcn_ballot_w64(ainc > x1);
+                if (!has_end) break;
+                if (hit1) {
+                    pick(endc, __builtin_ctzll(hit1), base, pre, cnt, L, n, incl, cinc);
+                    break;
+                }
             }
             pre += __builtin_amdgcn_readlane(incl, kWave - 1);
+            cnt += __builtin_amdgcn_readlane(cinc, kWave - 1);
         }
-        const int rem = g0 - cur.pre * Hkv;
-        cur.kvh = rem / cur.n;
-        cur.sub = rem - cur.kvh * cur.n;
     }
+    // position inside the sequence: KV head, then sub-tile past the ghosts
+    auto settle = [&](int64_t x, Cursor &u) -> int {
+        const int64_t rem = x - ((int64_t)u.pre + (int64_t)C * u.cnt) * Hkv;
+        u.kvh = (int)(rem / (u.n + C));
+        const int o = (int)(rem - (int64_t)u.kvh * (u.n + C)) - C;
+        u.sub = o > 0 ? o : 0;
+        return Hkv * u.pre + u.kvh * u.n + u.sub;
+    };
+    const int g0 = settle(x0, cur);
+    const int g1 = has_end ? settle(x1, endc) : T;
     auto advance = [&](Cursor &u) {
         if (++u.sub < u.n) return;
         u.sub = 0;
         if (++u.kvh < Hkv) return;
         u.kvh = 0;
         u.pre += u.n;
+        ++u.cnt;
         do {
             ++u.seq;
             u.L = tilesL(lens[u.seq]);
@@ -489,8 +510,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             write_out(u, acc, l_run);
             return;
         }
-        const int w_first = wave_of(ua);
-        const int w_last = wave_of(ub - 1);
+        // augmented position of the unit's first sub-tile, past its ghosts
+        const int64_t xa = ((int64_t)u.pre + (int64_t)C * u.cnt) * Hkv + (int64_t)u.kvh * (u.n + C) + C;
+        const int w_first = wave_of(xa);
+        const int w_last = wave_of(xa + u.n - 1);
         const int k = w_last - w_first + 1;
         const int unit = u.seq * Hkv + u.kvh;
         const int64_t base = (int64_t)w_first + unit;  // slots of this unit: base .. base + k - 1
