@@ -71,9 +71,10 @@ struct Cursor {
 };
 
 // ------------------------------------------------------------------ the kernel
-// No occupancy is forced on the compiler: squeezing the 16-bit, 4-head
-// configuration to 3 waves per SIMD makes it spill, and a kernel that uses
-// scratch streams ~20% slower than the spill-free one at 2 waves per SIMD.
+// No occupancy is forced on the compiler.  The 16-bit, 4-head configuration
+// at head_dim 128 takes about 260 registers and runs one wave per SIMD; held
+// to 256 it runs two without spilling, but measured slower (each wave's share
+// halves while the fixed costs of its segments stay), and at three it spills.
 template <typename DT, int D, int G>
 __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(DecodeArgs a) {
     constexpr int EB = DT::kBytes;
@@ -286,18 +287,20 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
 
     // ---- per-unit state
     u32x4 qr[NL];                 // B operand: head = lane % 16 (zero past G)
-    u32x4 knew[NL], vnew[NL];     // fused step: the appended token, row 0 of a one-row tile
     float m_run = kNegInf;        // lane (rg, j): running max of stream rg, head j (log2 units)
     float l_run = 0.f;            // its exp-sum
     float acc[G][NCH][VEC];       // lane (rg, c): un-normalised output of stream rg
     int seg_first = g0;           // first sub-tile of the current segment
 
-    auto start_unit = [&](const Cursor &u) {
+    // `knew` / `vnew` receive the appended token of a fused step (row 0 of a
+    // one-row tile) when `with_new`; the caller scopes them to the unit's
+    // start so that they are not live across the sub-tile loop.
+    auto start_unit = [&](const Cursor &u, bool with_new, u32x4 (&knew)[NL], u32x4 (&vnew)[NL]) {
         const char *qb = static_cast<const char *>(a.q) + uniform(((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW);
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, G * ROW, kBufferFlags);
         const int qoff = c * ROW + 16 * rg;  // head c (out of range, so zero, for c >= G)
         static_for<0, NL>([&]<int b>() { qr[b] = load_chunk(rq, qoff + 64 * b); });
-        if (fused && u.sub == 0) {
+        if (with_new) {
             // the new token as a one-row tile in the K and V layouts
             const int64_t nb = uniform(((int64_t)u.seq * Hkv + u.kvh) * ROW);
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -607,7 +610,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     };
     // Fused step, unit's first sub-tile: fold the appended token (position
     // L - 1 of the sequence) into the running state and store it in its slot.
-    auto fold_new_token = [&](const Cursor &u) {
+    auto fold_new_token = [&](const Cursor &u, const u32x4 (&knew)[NL], const u32x4 (&vnew)[NL]) {
         process_rows(1, knew, vnew);
         const int64_t so = uniform(slot_offset(u.seq, u.kvh, u.L));
         char *kd = static_cast<char *>(a.k_cache_w) + so;
@@ -641,8 +644,14 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     });
     int g = g0;
     while (true) {
-        start_unit(cp);
-        if (fused && cp.sub == 0) fold_new_token(cp);
+        if (fused && cp.sub == 0) {
+            u32x4 knew[NL], vnew[NL];
+            start_unit(cp, true, knew, vnew);
+            fold_new_token(cp, knew, vnew);
+        } else {
+            u32x4 knew[NL], vnew[NL];   // unused
+            start_unit(cp, false, knew, vnew);
+        }
         seg_first = g;
         int brk = 0;
         bool done = false;

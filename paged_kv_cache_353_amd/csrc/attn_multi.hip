@@ -50,6 +50,10 @@ constexpr int kDescWords = 8;     // unit descriptor: first slot, records, row, 
 constexpr int kColDescWords = 4;  // column descriptor: first slot, records, column in the record, flags
 constexpr int kHasPrefix = 1;     // flag of a suffix column descriptor: a prefix part exists
 constexpr float kLazyRescale = 8.f;  // headroom of the softmax reference (weights < 2^8)
+// Fixed cost of a segment (q loads, the column sums, the record), in
+// sub-tiles of streaming: the split charges it to the wave whose range holds
+// the start of a unit.
+constexpr int kUnitCost = 4;
 
 // Position of a wave's load or compute stage.  Every field is wave-uniform.
 struct MCursor {
@@ -231,10 +235,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         }
     }
 
-    // ---- total work and this wave's range (equal contiguous shares).  Up to
-    // kCachedBatches batches of 64 rows are read and scanned once, and the
-    // scans are kept for locating the wave's start; longer calls read the
-    // rows a second time.
+    // ---- total work and this wave's range.  In an augmented order every unit
+    // is preceded by C ghost positions that stand for the fixed cost of a
+    // segment; the augmented order is cut into equal ranges and a wave
+    // processes the real sub-tiles of its range, so a wave whose range holds
+    // unit starts streams fewer of them.  Up to kCachedBatches batches of 64
+    // rows are read and scanned once, and the scans are kept for locating the
+    // range; longer calls read the rows a second time.
     constexpr int kCachedBatches = 4;
     const bool cached = R <= kCachedBatches * kWave;
     int tlc[kCachedBatches], unc[kCachedBatches], inc[kCachedBatches], uinc[kCachedBatches];
@@ -278,18 +285,24 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     const bool too_many = units > a.max_units;
     if (wave == 0 && lane == 0) a.unit_desc[0] = too_many ? 0 : units;   // units the reduce pass visits
     if (too_many) return;
-    const int Weff = T < W ? T : W;
+    // Ghosts are used only when every range is longer than C, so that no
+    // range holds ghosts alone and every wave gets at least one sub-tile.
+    // Shared mode does without: every unit there leaves records anyway, and
+    // charging its short suffix units measured slower.
+    int C = mode == kModeMulti ? kUnitCost : 0;
+    if (((int64_t)T + (int64_t)C * units) / W < C + 1) C = 0;
+    const int64_t TA = (int64_t)T + (int64_t)C * units;   // augmented length
+    const int Weff = C > 0 ? W : (T < W ? T : W);
     if (wave >= Weff) return;
-    auto start_of = [&](int w) -> int { return (int)((int64_t)T * w / Weff); };
-    auto wave_of = [&](int x) -> int {  // the largest w with start_of(w) <= x
-        int w = (int)(((int64_t)x * Weff) / T);
-        w = min(max(w, 0), Weff - 1);
-        while (w + 1 < Weff && start_of(w + 1) <= x) ++w;
-        while (w > 0 && start_of(w) > x) --w;
-        return w;
+    const int64_t x0 = TA * wave / Weff;                   // this wave's augmented range
+    const int64_t x1 = TA * (wave + 1) / Weff;
+    const bool has_end = x1 < TA;
+    // the wave whose range holds augmented position x: the largest w with
+    // TA * w / Weff <= x
+    auto wave_of = [&](int64_t x) -> int {
+        const int64_t w = ((x + 1) * Weff - 1) / TA;
+        return (int)(w < Weff - 1 ? w : Weff - 1);
     };
-    const int g0 = start_of(wave);
-    const int g1 = start_of(wave + 1);
 
     auto load_row = [&](MCursor &u) {
         const RowInfo ri = row_info(u.row, ld_scalar);
@@ -299,56 +312,84 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         u.chunks = uniform((u.cols + UC - 1) / UC);
     };
 
-    // ---- locate g0: row (prefix scans of sub-tiles and units), then unit and sub-tile
-    MCursor cur{};
-    if (cached) {
-        bool found = false;
-        static_for<0, kCachedBatches>([&]<int b>() {
-            if (found) return;
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(inc[b] > g0);
-            if (hit) {
+    // ---- locate the range's ends: the row (prefix scans of augmented
+    // sub-tile counts), then unit and sub-tile of the first real sub-tile at
+    // or after x0, and the index of the first one at or after x1 (T past the
+    // end).  `tl` / `un` are the found row's sub-tiles and units.
+    struct Found { int row, pre, upre, tl, un; };
+    Found f0{}, f1{};
+    {
+        bool got0 = false, got1 = !has_end;
+        auto test = [&](int base, int pre, int upre, int incl, int uincl, int tl, int un) {
+            const int64_t ainc = (int64_t)(pre + incl) + (int64_t)C * (upre + uincl);
+            auto take = [&](Found &fd, uint64_t hit) {
                 const int f = __builtin_ctzll(hit);
-                cur.row = b * kWave + f;
-                cur.pre = __builtin_amdgcn_readlane(inc[b] - tlc[b], f);
-                cur.upre = __builtin_amdgcn_readlane(uinc[b] - unc[b], f);
-                found = true;
+                fd.row = base + f;
+                fd.pre = pre + __builtin_amdgcn_readlane(incl - tl, f);
+                fd.upre = upre + __builtin_amdgcn_readlane(uincl - un, f);
+                fd.tl = __builtin_amdgcn_readlane(tl, f);
+                fd.un = __builtin_amdgcn_readlane(un, f);
+            };
+            if (!got0) {
+                const uint64_t hit = __builtin_amdgcn_ballot_w64(ainc > x0);
+                if (hit) { take(f0, hit); got0 = true; }
             }
-        });
-    } else {
-        int pre = 0, upre = 0;
-        for (int base = 0; base < R; base += kWave) {
-            const int r = base + lane;
-            int tl = 0, un = 0;
-            if (r < R) {
-                const RowInfo ri = row_info(r, ld_vec);
-                const int n = tiles_of(ri);
-                un = n > 0 ? Hkv * chunks_of(ri) : 0;
-                tl = un * n;
+            if (!got1) {
+                const uint64_t hit = __builtin_amdgcn_ballot_w64(ainc > x1);
+                if (hit) { take(f1, hit); got1 = true; }
             }
-            const int incl = wave_incl_scan(tl, lane);
-            const int uincl = wave_incl_scan(un, lane);
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(pre + incl > g0);
-            if (hit) {
-                const int f = __builtin_ctzll(hit);
-                cur.row = base + f;
-                cur.pre = pre + __builtin_amdgcn_readlane(incl - tl, f);
-                cur.upre = upre + __builtin_amdgcn_readlane(uincl - un, f);
-                break;
+        };
+        if (cached) {
+            static_for<0, kCachedBatches>([&]<int b>() {
+                if (got0 && got1) return;
+                test(b * kWave, 0, 0, inc[b], uinc[b], tlc[b], unc[b]);
+            });
+        } else {
+            int pre = 0, upre = 0;
+            for (int base = 0; base < R && !(got0 && got1); base += kWave) {
+                const int r = base + lane;
+                int tl = 0, un = 0;
+                if (r < R) {
+                    const RowInfo ri = row_info(r, ld_vec);
+                    const int n = tiles_of(ri);
+                    un = n > 0 ? Hkv * chunks_of(ri) : 0;
+                    tl = un * n;
+                }
+                const int incl = wave_incl_scan(tl, lane);
+                const int uincl = wave_incl_scan(un, lane);
+                test(base, pre, upre, incl, uincl, tl, un);
+                pre += __builtin_amdgcn_readlane(incl, kWave - 1);
+                upre += __builtin_amdgcn_readlane(uincl, kWave - 1);
             }
-            pre += __builtin_amdgcn_readlane(incl, kWave - 1);
-            upre += __builtin_amdgcn_readlane(uincl, kWave - 1);
         }
     }
+    // index of the first real sub-tile at or after x in the found row; also
+    // its unit (within the row) and sub-tile
+    auto settle = [&](int64_t x, const Found &fd, int &uir, int &sub) -> int {
+        const int n = uniform(fd.tl / fd.un);
+        const int64_t rem = x - ((int64_t)uniform(fd.pre) + (int64_t)C * uniform(fd.upre));
+        uir = (int)(rem / (n + C));
+        const int o = (int)(rem - (int64_t)uir * (n + C)) - C;
+        sub = o > 0 ? o : 0;
+        return uniform(fd.pre) + uir * n + sub;
+    };
+    MCursor cur{};
+    int g0;
     {
-        cur.row = uniform(cur.row);
-        cur.pre = uniform(cur.pre);
-        cur.upre = uniform(cur.upre);
+        cur.row = uniform(f0.row);
+        cur.pre = uniform(f0.pre);
+        cur.upre = uniform(f0.upre);
         load_row(cur);
-        const int rem = g0 - cur.pre;
-        const int uir = rem / cur.n;
-        cur.sub = rem - uir * cur.n;
+        int uir, sub;
+        g0 = settle(x0, f0, uir, sub);
+        cur.sub = sub;
         cur.kvh = uir / cur.chunks;
         cur.chunk = uir - cur.kvh * cur.chunks;
+    }
+    int g1 = T;
+    if (has_end) {
+        int uir, sub;
+        g1 = settle(x1, f1, uir, sub);
     }
     auto advance = [&](MCursor &u) {
         if (++u.sub < u.n) return;
@@ -599,7 +640,9 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         const bool whole = seg_first == ua && g_last + 1 == ub;
         typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
         if (seg_first == ua) {
-            const int k = whole ? 1 : wave_of(ub - 1) - wave + 1;
+            // augmented position of the unit's last sub-tile: past the
+            // ghosts of every unit up to this one
+            const int k = whole ? 1 : wave_of((int64_t)ub - 1 + (int64_t)C * (unit + 1)) - wave + 1;
             if (mode == kModeMulti) {
                 if (lane == 0) {
                     int32_t *d = a.unit_desc + kDescWords * (1 + (int64_t)unit);
