@@ -295,15 +295,11 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // `knew` / `vnew` receive the appended token of a fused step (row 0 of a
     // one-row tile) when `with_new`; the caller scopes them to the unit's
     // start so that they are not live across the sub-tile loop.
-    auto load_q = [&](const Cursor &u) {
+    auto start_unit = [&](const Cursor &u, bool with_new, u32x4 (&knew)[NL], u32x4 (&vnew)[NL]) {
         const char *qb = static_cast<const char *>(a.q) + uniform(((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW);
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, G * ROW, kBufferFlags);
         const int qoff = c * ROW + 16 * rg;  // head c (out of range, so zero, for c >= G)
         static_for<0, NL>([&]<int b>() { qr[b] = load_chunk(rq, qoff + 64 * b); });
-    };
-    // `q_loaded`: q was requested earlier, ahead of the segment's first tiles
-    auto start_unit = [&](const Cursor &u, bool q_loaded, bool with_new, u32x4 (&knew)[NL], u32x4 (&vnew)[NL]) {
-        if (!q_loaded) load_q(u);
         if (with_new) {
             // the new token as a one-row tile in the K and V layouts
             const int64_t nb = uniform(((int64_t)u.seq * Hkv + u.kvh) * ROW);
@@ -315,8 +311,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             static_for<0, NL>([&]<int m>() { vnew[m] = load_chunk(rv, voff + 256 * m); });
         }
         // wait for q here, so that the sub-tile loop is entered with nothing
-        // but its own loads in flight (and, at the range's start, the tiles
-        // requested after q) and its waits stay exact
+        // but its own loads in flight and its waits stay exact
 #pragma unroll
         for (int b = 0; b < NL; ++b) asm volatile("" ::"v"(qr[b]));
         m_run = kNegInf;
@@ -638,12 +633,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     Cursor cp = cur;   // the sub-tile being consumed (g), in buffer 0 at a segment start
     Cursor cl = cur;   // the most recently issued sub-tile ...
     int gl = g0;       // ... and its index
-    // At the range's start every wave requests the same things at once.  The
-    // first segment's q (unless the segment opens a unit of a fused step,
-    // whose appended token is loaded with it) is requested ahead of the first
-    // kDepth tiles, so that waiting for it leaves them all in flight.
-    const bool early_q = !(fused && cur.sub == 0);
-    if (early_q) load_q(cur);
     issue(cl, true, kbuf[0], vbuf[0]);
     static_for<1, kDepth - 1>([&]<int m>() {
         const bool more = gl + 1 < g1;
@@ -653,26 +642,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         }
         issue(cl, more, kbuf[m], vbuf[m]);
     });
-    // the first inner step's load already issued (the range's first segment only)
-    int pre_issued = 0;
-    if (early_q) {
-        const bool more = gl + 1 < g1;
-        if (more) {
-            advance(cl);
-            ++gl;
-        }
-        issue(cl, more, kbuf[kDepth - 1], vbuf[kDepth - 1]);
-        pre_issued = 1;
-    }
     int g = g0;
     while (true) {
         if (fused && cp.sub == 0) {
             u32x4 knew[NL], vnew[NL];
-            start_unit(cp, false, true, knew, vnew);
+            start_unit(cp, true, knew, vnew);
             fold_new_token(cp, knew, vnew);
         } else {
             u32x4 knew[NL], vnew[NL];   // unused
-            start_unit(cp, pre_issued != 0, false, knew, vnew);
+            start_unit(cp, false, knew, vnew);
         }
         seg_first = g;
         int brk = 0;
@@ -681,16 +659,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             static_for<0, kDepth>([&]<int i>() {
                 if (done) return;
                 constexpr int nb = (i + kDepth - 1) % kDepth;
-                if (pre_issued != 0) {
-                    pre_issued = 0;
-                } else {
-                    const bool more = gl + 1 < g1;
-                    if (more) {
-                        advance(cl);
-                        ++gl;
-                    }
-                    issue(cl, more, kbuf[nb], vbuf[nb]);
+                const bool more = gl + 1 < g1;
+                if (more) {
+                    advance(cl);
+                    ++gl;
                 }
+                issue(cl, more, kbuf[nb], vbuf[nb]);
                 process(cp, kbuf[i], vbuf[i]);
                 if (cp.sub + 1 == cp.n || g + 1 == g1) {
                     brk = i;
