@@ -373,16 +373,29 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         sub = o > 0 ? o : 0;
         return uniform(fd.pre) + uir * n + sub;
     };
+    // Shared mode: a range end that falls inside a unit no longer than the
+    // average range moves to the nearer end of that unit (the later one on a
+    // tie), so that short units -- a sequence's own suffix -- are never split
+    // between waves: every piece of a unit costs a record and a segment.  The
+    // ends inside longer units stay where they are, so the closed-form owner
+    // of their sub-tiles still holds, and a short unit has one owner.  Two
+    // ends that move to the same place leave a wave without work.
+    const int64_t nshort = mode == kModeShared ? TA / Weff : 0;
+    auto round_end = [&](int g, int n, int sub) -> int {
+        if (sub == 0 || n > nshort) return g;
+        return 2 * sub < n ? g - sub : g + (n - sub);
+    };
     MCursor cur{};
-    int g0;
+    int g0, sub0, n0;
     {
         cur.row = uniform(f0.row);
         cur.pre = uniform(f0.pre);
         cur.upre = uniform(f0.upre);
         load_row(cur);
-        int uir, sub;
-        g0 = settle(x0, f0, uir, sub);
-        cur.sub = sub;
+        int uir;
+        g0 = settle(x0, f0, uir, sub0);
+        n0 = cur.n;
+        cur.sub = sub0;
         cur.kvh = uir / cur.chunks;
         cur.chunk = uir - cur.kvh * cur.chunks;
     }
@@ -390,6 +403,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
     if (has_end) {
         int uir, sub;
         g1 = settle(x1, f1, uir, sub);
+        g1 = round_end(g1, uniform(f1.tl / f1.un), sub);
     }
     auto advance = [&](MCursor &u) {
         if (++u.sub < u.n) return;
@@ -405,6 +419,18 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             load_row(u);
         } while (u.n == 0 && u.row + 1 < R);
     };
+    {
+        const int g0r = round_end(g0, n0, sub0);
+        if (g0r >= g1) return;
+        if (g0r < g0) {
+            cur.sub = 0;
+        } else if (g0r > g0) {
+            // the range starts at the next unit (it exists: g0r < g1 <= T)
+            cur.sub = cur.n - 1;
+            advance(cur);
+        }
+        g0 = g0r;
+    }
     auto unit_index = [&](const MCursor &u) { return u.upre + u.kvh * u.chunks + u.chunk; };
     auto unit_first = [&](const MCursor &u) { return u.pre + (u.kvh * u.chunks + u.chunk) * u.n; };
 
