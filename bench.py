@@ -7,7 +7,9 @@ same work as two launches (paged_kv_write, then paged_attn_decode) and the
 decode alone are timed for context.
 The default workload is the Llama-8B-shaped batch: 64 sequences with context
 lengths uniform in [128, 2048], 32 query / 8 KV heads, head_dim 128, block
-size 16, bf16, blocks shuffled through an 8192-block pool.
+size 16, bf16, blocks shuffled through an 8192-block pool.  After it, the same
+line reports the long-context batch (4 sequences of 128k to 1M tokens) through
+the same step, and several query tokens per sequence on the Llama-8B batch.
 
 Inputs are resident in HBM before timing starts.  Steps rotate over several
 copies of the pool so that the data a step reads was last touched several
@@ -167,6 +169,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the long-context step timed after the Llama-8B batch")
     ap.add_argument("--query-tokens", type=int, default=4,
                     help="also time several query tokens per sequence (Llama-8B batch; 0 = skip)")
     args = ap.parse_args()
@@ -333,6 +337,33 @@ def main() -> int:
             "entry_point": f"paged_attn_decode_multi ({T} query tokens per sequence, causal)",
             "us": round(multi_us, 3), "kv_gbs": round(kv_bytes / (multi_us * 1e-6) / 1e9, 2),
             "query_tokens_per_s": round(S * T / (multi_us * 1e-6), 1)}
+
+    if args.workload == "llama8b" and not args.no_long_context:
+        # The long-context batch (4 sequences of 128k to 1M tokens: 8 GB of
+        # K/V, far beyond the caches) through the same fused step, back to
+        # back on its one pool copy; the GPU tests check its outputs.
+        print("[bench] building workload long_context", file=sys.stderr, flush=True)
+        lc = build_workload("long_context", dev)
+        lws = torch.zeros(max(1, pkv.paged_attn_decode_workspace_size(
+            lc.num_seqs, lc.num_q_heads, lc.num_kv_heads, lc.head_dim, lc.block_size, lc.max_context_len)),
+            dtype=torch.uint8, device=dev)
+        lout = torch.empty_like(lc.q)
+
+        def long_step(s, o):
+            pkv.paged_decode_step(lout, lc.q, lc.k_new, lc.v_new, lc.k_cache, lc.v_cache, lc.block_tables,
+                                  lc.context_lens, lc.block_size, lc.scale, max_context_len=lc.max_context_len,
+                                  workspace=lws)
+        for _ in range(2):
+            long_step(None, None)
+        long_us = timed(long_step, 10)
+        lbytes = lc.kv_read_bytes()
+        extras["long_context_step"] = {
+            "workload": lc.name, "num_seqs": lc.num_seqs, "context_tokens": int(lc.lens.sum()),
+            "kv_read_bytes_per_step": lbytes, "steps": 10, "us": round(long_us, 3),
+            "kv_gbs": round(lbytes / (long_us * 1e-6) / 1e9, 2),
+            "pct_of_hbm_peak": round(100.0 * lbytes / (long_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "query_tokens_per_s": round(lc.num_seqs / (long_us * 1e-6), 1)}
+        del lc, lws, lout
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (launch_us * 1e-6) / 1e9
