@@ -3,18 +3,21 @@
 A step is one pass of the whole hot path over one batch: append each
 sequence's new token to the paged cache and decode attention of one query
 token per sequence over its cache, in one launch (paged_decode_step).  The
-same work as two launches (paged_kv_write, then paged_attn_decode) and the
-decode alone are timed for context.
-The default workload is the Llama-8B-shaped batch: 64 sequences with context
+headline workload is the Llama-8B-shaped batch: 64 sequences with context
 lengths uniform in [128, 2048], 32 query / 8 KV heads, head_dim 128, block
-size 16, bf16, blocks shuffled through an 8192-block pool.  After it, the same
-line reports the long-context batch (4 sequences of 128k to 1M tokens) through
-the same step, and several query tokens per sequence on the Llama-8B batch.
+size 16, bf16, blocks shuffled through an 8192-block pool.
+
+The same JSON line then reports every other workload through the same
+library calls: the tiny fp32 batch, the fp16 block-size sweep (16/32/64/128,
+with its one-token append), the shared-prefix batch (sharing-unaware decode
+and paged_attn_decode_shared), the long-context batch (128k to 1M tokens) and
+four query tokens per sequence on the Llama-8B batch.
 
 Inputs are resident in HBM before timing starts.  Steps rotate over several
-copies of the pool so that the data a step reads was last touched several
-steps (>1 GB of other traffic) earlier and has left the 256 MiB Infinity
-Cache: the timed bytes come from HBM.
+copies of the pool where one copy would fit in the 256 MiB Infinity Cache, so
+the bytes a step reads come from HBM.  Calls go to the C entry points with
+their arguments marshalled once per input copy, so the timed region holds the
+library's launches and not the Python binding's argument checks.
 
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -37,11 +40,14 @@ METRIC = "decode-attn KV-read GB/s and % of MI355X HBM peak; query tokens/s"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "paged_kv_cache_353_amd", "csrc")
 
-
 # Sources the one-query decode kernel (the roofline kernel) is built and
 # launched from: counter readings taken on another version of them are not
 # reported.
 STREAM_SOURCES = ["attn_decode.hip", "kv_write.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.cpp"]
+
+
+def say(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def source_digest() -> str:
@@ -122,18 +128,166 @@ def parity_check(inp, out, pairs):
     return worst
 
 
-def cpu_baseline(inp, budget_s: float):
-    """The fp64 oracle, as it stands, timed on this host's cores over whole
-    passes of the same workload (append of the step's tokens, then decode of
-    every sequence and query head), repeated until about budget_s seconds."""
+# ---------------------------------------------------------------------------
+# calls through the C entry points, arguments marshalled once per input copy
+# ---------------------------------------------------------------------------
+
+class Calls:
+    """Pre-marshalled C calls of one workload: one argument tuple per input
+    copy and call kind; each call checks the returned status."""
+
+    def __init__(self, sets, outs, workspace, stream, max_context_len):
+        from paged_kv_cache_353_amd import _lib
+        self.lib = _lib.load_library()
+        self.sets, self.outs = sets, outs
+        ws, nws = workspace.data_ptr(), workspace.numel()
+        st = stream.cuda_stream
+        self.step_args, self.decode_args, self.write_args = [], [], []
+        for s, o in zip(sets, outs):
+            S, Hq, D = s.q.shape
+            nb, Hkv, bs, _ = s.k_cache.shape
+            mb = s.block_tables.shape[1]
+            dt = _lib._dtype_code(s.q)
+            self.step_args.append((o.data_ptr(), s.q.data_ptr(), s.k_new.data_ptr(), s.v_new.data_ptr(),
+                                   s.k_cache.data_ptr(), s.v_cache.data_ptr(), s.block_tables.data_ptr(),
+                                   s.context_lens.data_ptr(), S, Hq, Hkv, D, bs, mb, nb, max_context_len,
+                                   s.scale, dt, ws, nws, st))
+            self.decode_args.append((o.data_ptr(), s.q.data_ptr(), s.k_cache.data_ptr(), s.v_cache.data_ptr(),
+                                     s.block_tables.data_ptr(), s.context_lens.data_ptr(), S, Hq, Hkv, D, bs,
+                                     mb, nb, max_context_len, s.scale, dt, ws, nws, st))
+            self.write_args.append((s.k_new.data_ptr(), s.v_new.data_ptr(), s.k_cache.data_ptr(),
+                                    s.v_cache.data_ptr(), s.slot_mapping.data_ptr(), S, Hkv, D, bs, nb,
+                                    Hkv * D, Hkv * D, dt, st))
+
+    def _ok(self, status, what):
+        if status != 0:
+            raise RuntimeError(f"{what} failed: {self.lib.pkv_status_string(status).decode()}")
+
+    def step(self, k):
+        self._ok(self.lib.paged_decode_step(*self.step_args[k % len(self.step_args)]), "paged_decode_step")
+
+    def decode(self, k):
+        self._ok(self.lib.paged_attn_decode(*self.decode_args[k % len(self.decode_args)]), "paged_attn_decode")
+
+    def write(self, k):
+        self._ok(self.lib.paged_kv_write(*self.write_args[k % len(self.write_args)]), "paged_kv_write")
+
+    def separate(self, k):
+        self.write(k)
+        self.decode(k)
+
+
+def timed(fn, n, stream):
+    """Average microseconds per call of fn(k), k = 0..n-1, back to back, with
+    events on the stream the kernels run on."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for k in range(n):
+        fn(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
+
+
+def per_call(fn, n, stream):
+    """p10 / median / p90 of per-call durations (an event pair around each call)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        ev[k][0].record(stream)
+        fn(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    each = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    pick = lambda f: round(each[min(len(each) - 1, int(f * (len(each) - 1) + 0.5))], 3)
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "calls": n}
+
+
+def rates(nbytes, us, seqs, query_tokens=1):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 3), "kv_gbs": round(gbs, 2), "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+            "query_tokens_per_s": round(seqs * query_tokens / (us * 1e-6), 1)}
+
+
+def setup(name, dev, nsets):
+    """Workload, its input copies, outputs, a zeroed workspace and the calls."""
+    import torch
+    import paged_kv_cache_353_amd as pkv
+    base = build_workload(name, dev)
+    sets = replicas(base, nsets)
+    S, Hq, Hkv, D = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_dim
+    maxL = base.max_context_len
+    ws = torch.zeros(max(1, pkv.paged_attn_decode_workspace_size(S, Hq, Hkv, D, base.block_size, maxL)),
+                     dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(s.q) for s in sets]
+    calls = Calls(sets, outs, ws, torch.cuda.current_stream(), maxL)
+    return base, sets, outs, ws, calls
+
+
+def workload_line(name, dev, steps, warmup, nsets, stream):
+    """Step, separate append + decode, decode alone and the append alone of
+    one workload, each back to back over its input copies."""
+    import torch
+    base, sets, outs, ws, calls = setup(name, dev, nsets)
+    for k in range(max(2, warmup)):
+        calls.step(k)
+    torch.cuda.synchronize()
+    step_us = timed(calls.step, steps, stream)
+    sep_us = timed(calls.separate, steps, stream)
+    dec_us = timed(calls.decode, steps, stream)
+    wr_us = timed(calls.write, steps, stream)
+    nbytes = base.kv_read_bytes()
+    line = {"workload": base.name, "num_seqs": base.num_seqs, "block_size": base.block_size,
+            "dtype": base.dtype, "context_tokens": int(base.lens.sum()), "kv_read_bytes_per_step": nbytes,
+            "input_sets": nsets, "steps": steps, **rates(nbytes, step_us, base.num_seqs),
+            "separate_write_then_decode_us": round(sep_us, 3), "decode_only_us": round(dec_us, 3),
+            "kv_write_us": round(wr_us, 3)}
+    del base, sets, outs, ws, calls
+    torch.cuda.empty_cache()
+    return line
+
+
+# ---------------------------------------------------------------------------
+# the CPU oracle on this host's cores
+# ---------------------------------------------------------------------------
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_oracle(inp, budget_s: float, seqs=None, heads=None, with_append=True):
+    """The fp64 oracle, as it stands, timed on this host over whole passes of
+    a bounded sample of the workload (the append of the sample's tokens, then
+    decode of the sampled sequences and query heads), repeated until about
+    budget_s seconds.  Rates are per query token and per algorithmic KV byte
+    of the sample, and the time of one whole step is extrapolated from them.
+    The oracle's append copies the whole pool, so for multi-GiB pools the
+    sample times the decode alone (with_append False)."""
     import numpy as np
     import oracle
     from paged_kv_cache_353_amd.workloads import to_numpy_bits
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    S, Hq = inp.num_seqs, inp.num_q_heads
+    seqs = list(range(S)) if seqs is None else list(seqs)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    pairs = [(i, h) for i in seqs for h in heads]
     q = to_numpy_bits(inp.q)
     kc = to_numpy_bits(inp.k_cache)
     vc = to_numpy_bits(inp.v_cache)
@@ -141,36 +295,47 @@ def cpu_baseline(inp, budget_s: float):
     tables = inp.block_tables.cpu().numpy()
     lens = inp.context_lens.cpu().numpy()
     slots = inp.slot_mapping.cpu().numpy()
+    sel = np.zeros(S, dtype=bool)
+    sel[seqs] = True
+    slots_s = np.where(sel, slots, -1)
+    whole = len(seqs) == S and len(heads) == Hq
     passes, t_total = 0, 0.0
     while passes == 0 or t_total < budget_s:
         t0 = time.perf_counter()
-        kc2, vc2 = oracle.paged_kv_write(kn, vn, kc, vc, slots)
-        oracle.paged_attn_decode(q, kc2, vc2, tables, lens, inp.block_size, inp.scale, inp.dtype)
+        kc2, vc2 = oracle.paged_kv_write(kn, vn, kc, vc, slots_s) if with_append else (kc, vc)
+        oracle.paged_attn_decode(q, kc2, vc2, tables, lens, inp.block_size, inp.scale, inp.dtype,
+                                 pairs=None if whole else pairs)
         t_total += time.perf_counter() - t0
         passes += 1
-    seqs = passes * inp.num_seqs
-    kv_bytes = passes * int(lens.sum()) * inp.num_kv_heads * inp.head_dim * 2 * (4 if inp.dtype == "f32" else 2)
-    return {"value": round(seqs / t_total, 2), "unit": "query tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": (f"{passes} whole pass(es) of the same workload ({inp.num_seqs} sequences, "
-                       f"all {inp.num_q_heads} query heads, append then decode) in {t_total:.1f} s; "
-                       f"{len(os.sched_getaffinity(0))} host cores visible"),
-            "kv_read_gbs": round(kv_bytes / t_total / 1e9, 4),
-            "seconds": round(t_total, 3)}
+    eb = 4 if inp.dtype == "f32" else 2
+    sample_tokens = int(lens[seqs].sum())
+    # a query token of the sample attends with len(heads) of its heads
+    frac_heads = len(heads) / Hq
+    sample_bytes = sample_tokens * inp.num_kv_heads * inp.head_dim * 2 * eb * frac_heads
+    t_pass = t_total / passes
+    all_bytes = int(lens.sum()) * inp.num_kv_heads * inp.head_dim * 2 * eb
+    t_step = t_pass * all_bytes / max(sample_bytes, 1.0)
+    return {"workload": inp.name,
+            "sample": (f"{passes} pass(es) of {'append + ' if with_append else ''}decode over {len(seqs)} of {S} "
+                       f"sequences x {len(heads)} of {Hq} query heads ({sample_tokens} context tokens) "
+                       f"in {t_total:.1f} s"),
+            "seconds_per_sample_pass": round(t_pass, 4), "step_seconds_extrapolated": round(t_step, 3),
+            "query_tokens_per_s": round(S / t_step, 3),
+            "kv_read_gbs": round(sample_bytes / t_pass / 1e9, 4)}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b", help="headline workload (the others follow as extras)")
     ap.add_argument("--sets", type=int, default=4, help="rotating input copies (cold-cache timing)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU oracle timing")
+    ap.add_argument("--cpu-budget", type=float, default=4.0, help="seconds of CPU oracle timing per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--no-long-context", action="store_true",
-                    help="skip the long-context step timed after the Llama-8B batch")
+    ap.add_argument("--no-extras", action="store_true", help="time the headline workload only")
+    ap.add_argument("--no-long-context", action="store_true", help="skip the long-context extra")
     ap.add_argument("--query-tokens", type=int, default=4,
                     help="also time several query tokens per sequence (Llama-8B batch; 0 = skip)")
     args = ap.parse_args()
@@ -192,126 +357,52 @@ def main() -> int:
     dev = "cuda:0"
     torch.cuda.set_device(0)
     pkv.load_library()
-    print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
-    base = build_workload(args.workload, dev)
+    stream = torch.cuda.current_stream()
+    K, Wm = args.steps, args.warmup
+
+    # ---- headline: the Llama-8B-shaped decode step
+    say(f"building workload {args.workload}")
     nsets = max(1, args.sets if args.workload != "long_context" else 1)
-    sets = replicas(base, nsets)
+    base, sets, outs, ws, calls = setup(args.workload, dev, nsets)
     S, Hq, Hkv, D = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_dim
     maxL = base.max_context_len
-    ws_bytes = pkv.paged_attn_decode_workspace_size(S, Hq, Hkv, D, base.block_size, maxL)
-    workspace = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    outs = [torch.empty_like(s.q) for s in sets]
     kv_bytes = base.kv_read_bytes()
     kv_unique = base.kv_unique_bytes()   # differs from kv_bytes only where blocks are shared
-    stream = torch.cuda.current_stream()
 
-    def step(s, out):
-        """One pass of the hot path: append + decode in one launch."""
-        pkv.paged_decode_step(out, s.q, s.k_new, s.v_new, s.k_cache, s.v_cache, s.block_tables,
-                              s.context_lens, s.block_size, s.scale, max_context_len=maxL,
-                              workspace=workspace)
-
-    def separate(s, out):
-        """The same step as two calls: paged_kv_write, then paged_attn_decode."""
-        pkv.paged_kv_write(s.k_new, s.v_new, s.k_cache, s.v_cache, s.slot_mapping)
-        pkv.paged_attn_decode(out, s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
-                              s.block_size, s.scale, max_context_len=maxL, workspace=workspace)
-
-    # parity of the timed data, before timing
-    step(sets[0], outs[0])
+    # parity of the timed data, before timing (the step appends the same
+    # bytes again on every later call, so the data stays the same)
+    calls.step(0)
     torch.cuda.synchronize()
     worst = None
     if not args.no_parity:
-        print("[bench] parity check on sampled outputs", file=sys.stderr, flush=True)
+        say("parity check on sampled outputs")
         pairs = [(i % S, (7 * i) % Hq) for i in range(0, S, max(1, S // 16))]
         worst = parity_check(sets[0], outs[0], pairs)
 
-    for k in range(args.warmup):
-        step(sets[k % nsets], outs[k % nsets])
+    # W untimed warmup steps, then more until the GPU has been busy for about
+    # 0.2 s, so that the timed steps do not run at idle clocks
+    for k in range(Wm):
+        calls.step(k)
     torch.cuda.synchronize()
-
-    def timed(fn, n):
-        """Average microseconds per call of fn over n calls back to back on
-        the rotating copies, with events on the stream the kernels run on."""
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.2:
+        for k in range(50):
+            calls.step(k)
         torch.cuda.synchronize()
-        e[0].record(stream)
-        for k in range(n):
-            fn(sets[k % nsets], outs[k % nsets])
-        e[1].record(stream)
-        torch.cuda.synchronize()
-        return e[0].elapsed_time(e[1]) / n * 1e3
-
-    K = args.steps
     w0 = time.perf_counter()
-    step_us = timed(step, K)          # the timed region: K steps
+    step_us = timed(calls.step, K, stream)          # the timed region: K steps
     wall = time.perf_counter() - w0
-    ms_step = step_us * 1e-3
-    launch_us = step_us               # one launch per step
-    separate_us = timed(separate, K)  # context: the same work as two launches
-    decode_only_us = timed(lambda s, o: pkv.paged_attn_decode(
-        o, s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens, s.block_size, s.scale,
-        max_context_len=maxL, workspace=workspace), K)
-
-    # per-call durations of the step on the rotating copies (an event pair
-    # around every call), for the spread: p10 / median / p90
-    n_each = min(K, 100)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_each)]
-    for k in range(n_each):
-        ev[k][0].record(stream)
-        step(sets[k % nsets], outs[k % nsets])
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    each = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-    pick = lambda f: round(each[min(len(each) - 1, int(f * (len(each) - 1) + 0.5))], 3)
-    step_spread = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "calls": n_each}
-
-    # warm (single set, back to back) step time, for context
-    warm = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    warm[0].record(stream)
-    for _ in range(20):
-        step(base, outs[0])
-    warm[1].record(stream)
-    torch.cuda.synchronize()
-    warm_us = warm[0].elapsed_time(warm[1]) / 20 * 1e3
+    separate_us = timed(calls.separate, K, stream)  # context: the same work as two launches
+    decode_only_us = timed(calls.decode, K, stream)
+    step_spread = per_call(calls.step, min(K, 100), stream)
+    # binding overhead, for context: the same step through the Python binding
+    binding_us = timed(lambda k: pkv.paged_decode_step(
+        outs[k % nsets], sets[k % nsets].q, sets[k % nsets].k_new, sets[k % nsets].v_new, sets[k % nsets].k_cache,
+        sets[k % nsets].v_cache, sets[k % nsets].block_tables, sets[k % nsets].context_lens, base.block_size,
+        base.scale, max_context_len=maxL, workspace=ws), K, stream)
+    warm_us = timed(lambda k: calls.step(0), 20, stream)   # one copy, back to back: cache-warm context
 
     extras = {}
-    if args.workload == "shared_prefix":
-        # the same decode with each group's shared prefix streamed once for
-        # all its forks (group description derived on the host, untimed)
-        from paged_kv_cache_353_amd.sharing import shared_prefix_groups
-        gs, pl = shared_prefix_groups(base.block_tables.cpu().numpy(), base.lens, base.block_size)
-        gs_d = torch.from_numpy(gs).to(dev)
-        pl_d = torch.from_numpy(pl).to(dev)
-        sws = torch.zeros(max(1, pkv.paged_attn_decode_shared_workspace_size(S, len(gs) - 1, Hq, Hkv, D)),
-                          dtype=torch.uint8, device=dev)
-        # the binding once for parity, then the C entry point with its
-        # arguments marshalled up front, so that the timing is the library's
-        # and not Python's (two launches per call)
-        pkv.paged_attn_decode_shared(outs[0], sets[0].q, sets[0].k_cache, sets[0].v_cache, sets[0].block_tables,
-                                     sets[0].context_lens, gs_d, pl_d, base.block_size, base.scale,
-                                     max_context_len=maxL, workspace=sws)
-        torch.cuda.synchronize()
-        if not args.no_parity:
-            parity_check(sets[0], outs[0], pairs)
-        lib = pkv.load_library()
-        sargs = {id(x): (o.data_ptr(), x.q.data_ptr(), x.k_cache.data_ptr(), x.v_cache.data_ptr(),
-                         x.block_tables.data_ptr(), x.context_lens.data_ptr(), gs_d.data_ptr(), pl_d.data_ptr(),
-                         S, len(gs) - 1, Hq, Hkv, D, base.block_size, x.block_tables.shape[1],
-                         x.k_cache.shape[0], maxL, base.scale, _lib._dtype_code(x.q), sws.data_ptr(), sws.numel(),
-                         stream.cuda_stream) for x, o in zip(sets, outs)}
-
-        def shared_call(s, o):
-            if lib.paged_attn_decode_shared(*sargs[id(s)]) != 0:
-                raise RuntimeError("paged_attn_decode_shared failed")
-        shared_us = timed(shared_call, K)
-        extras["shared_prefix_decode"] = {
-            "entry_point": "paged_attn_decode_shared (each group's prefix streamed once with its members' heads as columns, suffixes per sequence; one streaming launch plus a reduce launch)",
-            "groups": len(gs) - 1, "shared_tokens_per_group": int(pl[0]),
-            "us": round(shared_us, 3),
-            "unique_kv_gbs": round(kv_unique / (shared_us * 1e-6) / 1e9, 2),
-            "logical_kv_gbs": round(kv_bytes / (shared_us * 1e-6) / 1e9, 2),
-            "speedup_vs_decode_only": round(decode_only_us / shared_us, 3)}
     if args.workload == "llama8b" and args.query_tokens > 0:
         # several query tokens per sequence (draft verification) on the same batch
         from paged_kv_cache_353_amd.workloads import multi_query
@@ -320,95 +411,155 @@ def main() -> int:
         o4s = [torch.empty_like(x) for x in q4s]
         mws = torch.zeros(max(1, pkv.paged_attn_decode_multi_workspace_size(S, T, Hq, Hkv, D)),
                           dtype=torch.uint8, device=dev)
-        pkv.paged_attn_decode_multi(o4s[0], q4s[0], sets[0].k_cache, sets[0].v_cache, sets[0].block_tables,
-                                    sets[0].context_lens, base.block_size, base.scale, max_context_len=maxL,
-                                    workspace=mws)
-        lib = pkv.load_library()
-        margs = {id(x): (o4.data_ptr(), q4.data_ptr(), x.k_cache.data_ptr(), x.v_cache.data_ptr(),
-                         x.block_tables.data_ptr(), x.context_lens.data_ptr(), S, T, Hq, Hkv, D, base.block_size,
-                         x.block_tables.shape[1], x.k_cache.shape[0], maxL, base.scale, _lib._dtype_code(x.q),
-                         mws.data_ptr(), mws.numel(), stream.cuda_stream) for x, q4, o4 in zip(sets, q4s, o4s)}
+        lib = calls.lib
+        margs = [(o4.data_ptr(), q4.data_ptr(), x.k_cache.data_ptr(), x.v_cache.data_ptr(),
+                  x.block_tables.data_ptr(), x.context_lens.data_ptr(), S, T, Hq, Hkv, D, base.block_size,
+                  x.block_tables.shape[1], x.k_cache.shape[0], maxL, base.scale, _lib._dtype_code(x.q),
+                  mws.data_ptr(), mws.numel(), stream.cuda_stream) for x, q4, o4 in zip(sets, q4s, o4s)]
 
-        def multi_call(s, o):
-            if lib.paged_attn_decode_multi(*margs[id(s)]) != 0:
+        def multi_call(k):
+            if lib.paged_attn_decode_multi(*margs[k % nsets]) != 0:
                 raise RuntimeError("paged_attn_decode_multi failed")
-        multi_us = timed(multi_call, K)
+        for k in range(3):
+            multi_call(k)
+        multi_us = timed(multi_call, K, stream)
         extras["multi_query_decode"] = {
             "entry_point": f"paged_attn_decode_multi ({T} query tokens per sequence, causal)",
-            "us": round(multi_us, 3), "kv_gbs": round(kv_bytes / (multi_us * 1e-6) / 1e9, 2),
-            "query_tokens_per_s": round(S * T / (multi_us * 1e-6), 1)}
+            **rates(kv_bytes, multi_us, S, T)}
+        del q4s, o4s, mws
 
-    if args.workload == "llama8b" and not args.no_long_context:
-        # The long-context batch (4 sequences of 128k to 1M tokens: 8 GB of
-        # K/V, far beyond the caches) through the same fused step, back to
-        # back on its one pool copy; the GPU tests check its outputs.
-        print("[bench] building workload long_context", file=sys.stderr, flush=True)
-        lc = build_workload("long_context", dev)
-        lws = torch.zeros(max(1, pkv.paged_attn_decode_workspace_size(
-            lc.num_seqs, lc.num_q_heads, lc.num_kv_heads, lc.head_dim, lc.block_size, lc.max_context_len)),
-            dtype=torch.uint8, device=dev)
-        lout = torch.empty_like(lc.q)
+    head_name, head_seqs = base.name, S
+    del sets, outs, ws, calls
+    torch.cuda.empty_cache()
 
-        def long_step(s, o):
-            pkv.paged_decode_step(lout, lc.q, lc.k_new, lc.v_new, lc.k_cache, lc.v_cache, lc.block_tables,
-                                  lc.context_lens, lc.block_size, lc.scale, max_context_len=lc.max_context_len,
-                                  workspace=lws)
-        for _ in range(2):
-            long_step(None, None)
-        long_us = timed(long_step, 10)
-        lbytes = lc.kv_read_bytes()
-        extras["long_context_step"] = {
-            "workload": lc.name, "num_seqs": lc.num_seqs, "context_tokens": int(lc.lens.sum()),
-            "kv_read_bytes_per_step": lbytes, "steps": 10, "us": round(long_us, 3),
-            "kv_gbs": round(lbytes / (long_us * 1e-6) / 1e9, 2),
-            "pct_of_hbm_peak": round(100.0 * lbytes / (long_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
-            "query_tokens_per_s": round(lc.num_seqs / (long_us * 1e-6), 1)}
-        del lc, lws, lout
+    if not args.no_extras and args.workload == "llama8b":
+        ext = {}
+        say("workload tiny")
+        ext["tiny_fp32"] = workload_line("tiny", dev, K, Wm, 1, stream)
+        for bs in (16, 32, 64, 128):
+            say(f"workload sweep bs {bs}")
+            ext[f"sweep_fp16_bs{bs}"] = workload_line(f"sweep{bs}", dev, max(10, K // 2), Wm, 2, stream)
+        say("workload shared prefix")
+        sp = workload_line("shared_prefix", dev, K, Wm, 4, stream)
+        sp.update(shared_prefix_line(dev, K, stream))
+        ext["shared_prefix_bf16"] = sp
+        if not args.no_long_context:
+            say("workload long context")
+            ext["long_context_bf16"] = workload_line("long_context", dev, 10, 2, 1, stream)
+        extras["workloads"] = ext
 
-    value = kv_bytes / (ms_step * 1e-3) / 1e9
-    achieved = kv_bytes / (launch_us * 1e-6) / 1e9
-    traffic = traffic_for(base.name)
+    value = kv_bytes / (step_us * 1e-6) / 1e9
+    traffic = traffic_for(head_name)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "warmup": Wm,
+        "ms_per_step": round(step_us * 1e-3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": base.dtype,
         "data": "synthetic (seeded N(0,1) values, shuffled block tables; no dataset)",
-        "config": {"workload": base.name, "num_seqs": S, "num_q_heads": Hq,
+        "config": {"workload": head_name, "num_seqs": S, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": base.block_size,
                    "context_tokens": int(base.lens.sum()), "max_context_len": maxL,
                    "kv_read_bytes_per_step": kv_bytes, "kv_unique_bytes_per_step": kv_unique,
                    "input_sets": nsets},
-        "query_tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "query_tokens_per_s": round(head_seqs / (step_us * 1e-6), 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "unique_kv_gbs": round(kv_unique / (ms_step * 1e-3) / 1e9, 2),
-        "step_launch_us": round(launch_us, 3),
+        "unique_kv_gbs": round(kv_unique / (step_us * 1e-6) / 1e9, 2),
+        "step_launch_us": round(step_us, 3),
         "separate_write_then_decode_us": round(separate_us, 3),
         "decode_only_us": round(decode_only_us, 3),
+        "python_binding_step_us": round(binding_us, 3),
         "warm_step_us": round(warm_us, 3),
         "step_us_per_call": step_spread,
         "wall_s": round(wall, 4),
         "roofline": {"bound": "hbm", "kernel": "attn_stream_kernel (paged_decode_step: append + decode, one launch)",
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+                     "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic},
         "parity_worst_normwise": worst,
         **extras,
         "kernel_source": source_digest(),
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(base, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baselines(dev, args.cpu_budget, args.no_extras or args.workload != "llama8b",
+                                               args.workload)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
     return 0
+
+
+def shared_prefix_line(dev, steps, stream):
+    """paged_attn_decode_shared on the forked batch: each group's prefix read
+    once for all its members (group description derived on the host, untimed)."""
+    import torch
+    import paged_kv_cache_353_amd as pkv
+    from paged_kv_cache_353_amd import _lib
+    from paged_kv_cache_353_amd.sharing import shared_prefix_groups
+    base = build_workload("shared_prefix", dev)
+    sets = replicas(base, 4)
+    S, Hq, Hkv, D = base.num_seqs, base.num_q_heads, base.num_kv_heads, base.head_dim
+    maxL = base.max_context_len
+    gs, pl = shared_prefix_groups(base.block_tables.cpu().numpy(), base.lens, base.block_size)
+    gs_d = torch.from_numpy(gs).to(dev)
+    pl_d = torch.from_numpy(pl).to(dev)
+    sws = torch.zeros(max(1, pkv.paged_attn_decode_shared_workspace_size(S, len(gs) - 1, Hq, Hkv, D)),
+                      dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(s.q) for s in sets]
+    lib = _lib.load_library()
+    sargs = [(o.data_ptr(), x.q.data_ptr(), x.k_cache.data_ptr(), x.v_cache.data_ptr(),
+              x.block_tables.data_ptr(), x.context_lens.data_ptr(), gs_d.data_ptr(), pl_d.data_ptr(),
+              S, len(gs) - 1, Hq, Hkv, D, base.block_size, x.block_tables.shape[1],
+              x.k_cache.shape[0], maxL, base.scale, _lib._dtype_code(x.q), sws.data_ptr(), sws.numel(),
+              stream.cuda_stream) for x, o in zip(sets, outs)]
+
+    def shared_call(k):
+        if lib.paged_attn_decode_shared(*sargs[k % 4]) != 0:
+            raise RuntimeError("paged_attn_decode_shared failed")
+    for k in range(3):
+        shared_call(k)
+    torch.cuda.synchronize()
+    us = timed(shared_call, steps, stream)
+    nbytes, unique = base.kv_read_bytes(), base.kv_unique_bytes()
+    line = {"shared_decode": {
+        "entry_point": "paged_attn_decode_shared (each group's prefix streamed once for all its members)",
+        "groups": len(gs) - 1, "shared_tokens_per_group": int(pl[0]), "us": round(us, 3),
+        "unique_kv_bytes": unique, "unique_kv_gbs": round(unique / (us * 1e-6) / 1e9, 2),
+        "unique_pct_of_hbm_peak": round(100.0 * unique / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+        "logical_kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 2),
+        "query_tokens_per_s": round(S / (us * 1e-6), 1)}}
+    del base, sets, outs, sws
+    torch.cuda.empty_cache()
+    return line
+
+
+def cpu_baselines(dev, budget, headline_only, headline):
+    """The oracle on this host's cores: the headline workload first, then the
+    others on bounded samples; one entry per workload."""
+    import torch
+    say("timing the CPU oracle on bounded samples")
+    cores = len(os.sched_getaffinity(0))
+    entries = {}
+    plan = [(headline, None, None, True)]
+    if not headline_only:
+        plan += [("tiny", None, None, True),
+                 ("sweep16", range(0, 128, 16), None, False),       # 8 of 128 sequences, all heads
+                 ("shared_prefix", range(0, 128, 16), None, True),  # one sample of each of 8 prompts
+                 ("long_context", [0], range(0, 32, 8), False)]      # the 128k sequence, 4 of 32 heads
+    for name, seqs, heads, app in plan:
+        inp = build_workload(name, dev)
+        entries[inp.name] = cpu_oracle(inp, budget, seqs, heads, app)
+        del inp
+        torch.cuda.empty_cache()
+    head = next(iter(entries.values()))
+    return {"value": head["query_tokens_per_s"], "unit": "query tokens/s", "cores": cores, "kind": "oracle",
+            "sample": head["sample"], "cpu_model": cpu_model(), "blas_threads": blas_threads(),
+            "kv_read_gbs": head["kv_read_gbs"], "per_workload": entries}
 
 
 if __name__ == "__main__":

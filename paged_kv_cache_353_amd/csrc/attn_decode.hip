@@ -14,22 +14,26 @@
 // Work split (one launch).  A unit is one (sequence, KV head) pair; its work
 // is ceil(L/16) sub-tiles of 16 tokens.  All sub-tiles of all units, in
 // (sequence, KV head, position) order, are cut into W contiguous ranges, one
-// per wave, W being what the GPU holds at once.  The cut is even once every
-// unit is charged a few sub-tiles more for the fixed cost of starting and
-// finishing it, so every wave takes about the same time whatever the length
-// mix, with no empty workgroups and no tail of short partitions.  A unit that lies wholly inside
-// one wave's range is finished by that wave; a unit shared by k waves gets k
-// partial results (max, exp-sum, un-normalised output) in the workspace, and
-// the wave that arrives last at the unit's counter merges them in a fixed
-// order and writes the output.  The counter is reset to zero by that wave, so
-// the workspace is left as it was found.
+// per wave, W being what the GPU holds at once (one wave per SIMD).  The cut
+// is even once every unit is charged a few sub-tiles more for the fixed cost
+// of starting and finishing it, so every wave takes about the same time
+// whatever the length mix, with no empty workgroups and no tail of short
+// partitions.  A unit that lies wholly inside one wave's range is finished by
+// that wave; a unit shared by k waves gets k partial results (max, exp-sum,
+// un-normalised output) in the workspace, and the wave that arrives last at
+// the unit's counter merges them in a fixed order and writes the output.  The
+// counter is reset to zero by that wave, so the workspace is left as it was
+// found.  A wave reports the arrival of its first segment one sub-tile after
+// writing its record, without waiting for the count, and acts on the count at
+// the end of its range: the boundary costs the stream no round trip.
 //
 // One wave, one sub-tile (16 tokens of one KV head, the G query heads that
 // share it):
 //  * K and V rows come in with 16-byte raw buffer loads whose descriptor spans
 //    only the sub-tile's valid rows: tail rows of the last block read as zero
-//    and are never fetched.  The next sub-tile's loads are issued before the
-//    current one is consumed.
+//    and are never fetched.  The loads are marked non-temporal (read once).
+//    The next sub-tile's loads are issued before the current one is consumed,
+//    and the next unit's q before its unit's last sub-tile.
 //  * q.K is one 16x16 MFMA product per 32 (bf16/fp16) or 4 (fp32) dims: the
 //    16 tokens are the rows, the query heads the columns (up to 16, so any
 //    group size fits).  Lane (r, j) receives the scores of tokens 4r..4r+3 of
@@ -41,6 +45,10 @@
 //  * The lanes of row group r also hold V rows 4r..4r+3; probabilities and
 //    rescale factors reach them by DPP row broadcast, and acc += p V runs on
 //    the VALU in fp32.
+//  * In a fused step (append + decode) the appended token is the last row of
+//    the unit's last sub-tile: its K and V rows are loaded from k_new / v_new
+//    into the lanes that hold that row, and those lanes also store it into its
+//    slot.  The arithmetic is then the same as a decode after a separate append.
 //  * The summation order depends only on logical token positions and on the
 //    sizes of the problem, so results are bitwise reproducible and independent
 //    of where the blocks live physically or how large the blocks are.
@@ -52,11 +60,17 @@ namespace pkv {
 namespace {
 
 constexpr int kDirectMerge = 8;  // units split in at most this many pieces merge in one level
-constexpr int kDepth = 2;        // sub-tiles in flight per wave
-// Fixed cost of a segment (loading q, the lane reductions, the partial record
-// and its arrival), in sub-tiles of streaming.  The split charges it to the
-// wave whose range holds the start of a unit.
-constexpr int kUnitCost = 4;
+// Fixed cost of a segment (the lane reductions and the partial record or
+// output), in sub-tiles of streaming.  The split charges it to the wave whose
+// range holds the start of a unit.
+#ifndef PKV_UNIT_COST
+#define PKV_UNIT_COST 3
+#endif
+constexpr int kUnitCost = PKV_UNIT_COST;
+#ifndef PKV_DEPTH
+#define PKV_DEPTH 2
+#endif
+constexpr int kDepth = PKV_DEPTH;  // sub-tiles in flight per wave
 
 // Position of a wave's load or compute stage in the (sequence, KV head,
 // sub-tile) order.  Every field is wave-uniform.
@@ -65,16 +79,16 @@ struct Cursor {
     int kvh;   // KV head
     int sub;   // sub-tile inside the unit
     int n;     // sub-tiles of the unit
-    int L;     // tokens of the sequence read from the cache
+    int L;     // tokens the sequence attends to
     int pre;   // sub-tiles of one KV head summed over the sequences before `seq`
     int cnt;   // sequences before `seq` with at least one sub-tile
 };
 
 // ------------------------------------------------------------------ the kernel
-// No occupancy is forced on the compiler.  The 16-bit, 4-head configuration
-// at head_dim 128 takes about 260 registers and runs one wave per SIMD; held
-// to 256 it runs two without spilling, but measured slower (each wave's share
-// halves while the fixed costs of its segments stay), and at three it spills.
+// No occupancy is forced on the compiler: the 16-bit, 4-head configuration at
+// head_dim 128 runs one wave per SIMD.  Two per SIMD (held to 256 registers)
+// measured slower: the older wave of each SIMD takes the memory pipeline and
+// the younger one finishes its equal share long after it.
 template <typename DT, int D, int G>
 __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(DecodeArgs a) {
     constexpr int EB = DT::kBytes;
@@ -95,47 +109,19 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     const int W = a.num_waves;
     const const_i32_ptr lens = (const_i32_ptr)a.context_lens;
     auto clampL = [&](int L) { L = L < Lmax ? L : Lmax; return L > 0 ? L : 0; };
-    // A fused step appends each sequence's new token at position L - 1 and
-    // takes it from k_new / v_new rather than from the cache: the cache tiles
-    // cover [0, L - 1) and the new token is folded in once per unit.
+    // A fused step appends each sequence's new token at position L - 1: the
+    // cache holds positions [0, L - 1) and the token itself comes from
+    // k_new / v_new, into the registers of the unit's last sub-tile.
     const bool fused = a.k_new != nullptr;
     const int fused_one = fused ? 1 : 0;
-    auto tilesL = [&](int L) {  // tokens read from the cache: L - 1 in a fused step (L >= 1)
-        L = clampL(L);
-        return L - min(L, fused_one);
-    };
-    auto slot_offset = [&](int seq, int kvh, int pos) -> int64_t {  // bytes into a cache
-        const const_i32_ptr table = (const_i32_ptr)(a.block_tables + (int64_t)seq * a.max_blocks_per_seq);
-        const int j = pos / BS;
-        return (((int64_t)table[j] * Hkv + kvh) * BS + (pos - j * BS)) * (int64_t)ROW;
-    };
 
-    // ---- contexts with no cached token: the output is the empty sum, or in a
-    // fused step with one token, that token's value (its weight is 1); the
-    // new token is also written to its slot
-    for (int i = wave; i < S; i += W) {
-        const int L = clampL(lens[i]);
-        if (L == 0) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            char *o = static_cast<char *>(a.out) + (int64_t)i * Hq * ROW;
-            for (int off = lane * 16; off < Hq * ROW; off += kWave * 16)
-                *reinterpret_cast<u32x4 *>(o + off) = z;
-        } else if (fused && L == 1) {
-            for (int idx = lane; idx < Hkv * R; idx += kWave) {
-                const int g = idx / R, ch = idx - g * R;
-                const int64_t src = ((int64_t)i * Hkv + g) * ROW + ch * 16;
-                const u32x4 kx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.k_new) + src);
-                const u32x4 vx = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.v_new) + src);
-                const int64_t dst = slot_offset(i, g, 0) + ch * 16;
-                *reinterpret_cast<u32x4 *>(static_cast<char *>(a.k_cache_w) + dst) = kx;
-                *reinterpret_cast<u32x4 *>(static_cast<char *>(a.v_cache_w) + dst) = vx;
-                static_for<0, G>([&]<int h>() {
-                    *reinterpret_cast<u32x4 *>(static_cast<char *>(a.out) +
-                                               ((int64_t)i * Hq + (int64_t)g * G + h) * ROW + ch * 16) = vx;
-                });
-            }
-        }
-    }
+    // contexts with no token: the output is the empty sum (sequence i is
+    // written by wave i % W)
+    auto zero_out = [&](int i) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        char *o = static_cast<char *>(a.out) + (int64_t)i * Hq * ROW;
+        for (int off = lane * 16; off < Hq * ROW; off += kWave * 16) store_chunk(o, Hq * ROW, off, z);
+    };
 
     // ---- total work and this wave's range.  Sub-tiles are ordered (sequence,
     // KV head, position); a unit is a (sequence, KV head) pair with n >= 1 of
@@ -149,7 +135,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     int N = 0, NU = 0;   // sub-tiles of one KV head, and sequences with any
     int L0 = 0, n0 = 0, incl0 = 0, cinc0 = 0;
     if (one_batch) {
-        L0 = lane < S ? tilesL(a.context_lens[lane]) : 0;
+        L0 = lane < S ? clampL(a.context_lens[lane]) : 0;
+        if (wave < S && __builtin_amdgcn_readlane(L0, wave) == 0) zero_out(wave);
         n0 = (L0 + 15) >> 4;
         incl0 = wave_incl_scan(n0, lane);
         cinc0 = wave_incl_scan(n0 > 0 ? 1 : 0, lane);
@@ -158,12 +145,14 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     } else {
         for (int base = 0; base < S; base += kWave) {
             const int i = base + lane;
-            const int L = i < S ? tilesL(a.context_lens[i]) : 0;
+            const int L = i < S ? clampL(a.context_lens[i]) : 0;
             N += (L + 15) >> 4;
             NU += L > 0 ? 1 : 0;
         }
         N = uniform(wave_sum_i(N, lane));
         NU = uniform(wave_sum_i(NU, lane));
+        for (int i = wave; i < S; i += W)
+            if (clampL(lens[i]) == 0) zero_out(i);
     }
     // sub-tile indices fit in 32 bits (the host rejects larger batches);
     // augmented positions and products with a wave count take 64 bits
@@ -206,7 +195,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         bool found0 = false;
         for (int base = 0; base < S; base += kWave) {
             const int i = base + lane;
-            const int L = i < S ? tilesL(a.context_lens[i]) : 0;
+            const int L = i < S ? clampL(a.context_lens[i]) : 0;
             const int n = (L + 15) >> 4;
             const int incl = wave_incl_scan(n, lane);
             const int cinc = wave_incl_scan(n > 0 ? 1 : 0, lane);
@@ -238,7 +227,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     };
     const int g0 = settle(x0, cur);
     const int g1 = has_end ? settle(x1, endc) : T;
-    auto advance = [&](Cursor &u) {
+    auto advance = [&](Cursor &u) __attribute__((always_inline)) {
         if (++u.sub < u.n) return;
         u.sub = 0;
         if (++u.kvh < Hkv) return;
@@ -247,10 +236,11 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         ++u.cnt;
         do {
             ++u.seq;
-            u.L = tilesL(lens[u.seq]);
+            u.L = clampL(lens[u.seq]);
         } while (u.L == 0);
         u.n = (u.L + 15) >> 4;
     };
+    auto unit_of = [&](const Cursor &u) { return u.seq * Hkv + u.kvh; };
 
     const char *kc = static_cast<const char *>(a.k_cache);
     const char *vc = static_cast<const char *>(a.v_cache);
@@ -262,58 +252,69 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     const int koff = c * ROW + 16 * rg;
     const int voff = (4 * rg + (c / R)) * ROW + (c % R) * 16;
 
-    // Issues the K and V loads of the sub-tile at `u`; `live` false gives an
-    // empty range (loads return zeros and touch no memory), which keeps the
-    // number of loads in flight the same on every iteration.
-    auto issue = [&](const Cursor &u, bool live, u32x4 (&kr)[NL], u32x4 (&vr)[NL]) {
-        const int t0 = u.sub << 4;
+    // bytes from a cache's base to the first row of the sub-tile at `u`
+    auto tile_offset = [&](const Cursor &u) __attribute__((always_inline)) -> int64_t {
         const int j = u.sub / subs_per_block;
-        const int row0 = t0 - j * BS;
-        int rows = u.L - t0;
-        rows = rows < 16 ? rows : 16;
-        rows = live ? rows : 0;
         const const_i32_ptr table = (const_i32_ptr)(a.block_tables + (int64_t)u.seq * a.max_blocks_per_seq);
         const int64_t phys = table[j];
-        const int64_t off = uniform(phys * block_bytes + (int64_t)u.kvh * head_bytes + (int64_t)row0 * ROW);
+        return uniform(phys * block_bytes + (int64_t)u.kvh * head_bytes + (int64_t)((u.sub << 4) - j * BS) * ROW);
+    };
+    // the sub-tile at `u` ends the unit and holds the appended token of a fused step
+    auto holds_new = [&](const Cursor &u) { return fused && u.sub + 1 == u.n; };
+
+    // Issues the K and V loads of the sub-tile at `u`; `live` false gives an
+    // empty range (loads return zeros and touch no memory), which keeps the
+    // number of loads in flight the same on every step.  The descriptors span
+    // only the cached rows of the sub-tile, so rows past them read as zero.
+    auto issue = [&](const Cursor &u, bool live, u32x4 (&kr)[NL], u32x4 (&vr)[NL]) __attribute__((always_inline)) {
+        const int t0 = u.sub << 4;
+        int rows = u.L - fused_one - t0;
+        rows = rows < 16 ? rows : 16;
+        rows = rows > 0 ? rows : 0;
+        rows = live ? rows : 0;
+        const int64_t off = tile_offset(u);
         const int nbytes = uniform(rows * ROW);
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kc + off), 0, nbytes, kBufferFlags);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vc + off), 0, nbytes, kBufferFlags);
-        static_for<0, NL>([&]<int b>() { kr[b] = load_chunk(rk, koff + 64 * b); });
-        static_for<0, NL>([&]<int m>() { vr[m] = load_chunk(rv, voff + 256 * m); });
+        static_for<0, NL>([&]<int b>() { kr[b] = load_stream(rk, koff + 64 * b); });
+        static_for<0, NL>([&]<int m>() { vr[m] = load_stream(rv, voff + 256 * m); });
         // keep the compute of the previous sub-tile (and its waits) after these
         // loads, so that they are in flight while it runs
         __builtin_amdgcn_sched_barrier(0);
     };
+    // In a fused step the unit's last sub-tile takes the appended token's row
+    // from k_new / v_new: every lane loads through a descriptor that covers
+    // just that row, at an offset that lands inside it only in the lanes that
+    // hold the row (the others read zeros), and the result is OR-ed over the
+    // zeros the cache descriptor returned for that row.
+    u32x4 knew[NL], vnew[NL];
+    auto issue_new = [&](const Cursor &u) __attribute__((always_inline)) {
+        const int rn = u.L - 1 - (u.sub << 4);   // row of the appended token
+        const int64_t nb = uniform(((int64_t)u.seq * Hkv + u.kvh) * ROW);
+        const __amdgpu_buffer_rsrc_t rkn = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(static_cast<const char *>(a.k_new) + nb), 0, ROW, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rvn = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(static_cast<const char *>(a.v_new) + nb), 0, ROW, kBufferFlags);
+        // out-of-range offsets (negative ones wrap to huge) read as zero
+        static_for<0, NL>([&]<int b>() { knew[b] = load_chunk(rkn, koff - rn * ROW + 64 * b); });
+        static_for<0, NL>([&]<int m>() { vnew[m] = load_chunk(rvn, voff - rn * ROW + 256 * m); });
+    };
 
     // ---- per-unit state
     u32x4 qr[NL];                 // B operand: head = lane % 16 (zero past G)
+    u32x4 qn[NL];                 // the next unit's, requested ahead
+    int qn_unit = -1;             // unit whose q sits in qn
     float m_run = kNegInf;        // lane (rg, j): running max of stream rg, head j (log2 units)
     float l_run = 0.f;            // its exp-sum
     float acc[G][NCH][VEC];       // lane (rg, c): un-normalised output of stream rg
-    int seg_first = g0;           // first sub-tile of the current segment
 
-    // `knew` / `vnew` receive the appended token of a fused step (row 0 of a
-    // one-row tile) when `with_new`; the caller scopes them to the unit's
-    // start so that they are not live across the sub-tile loop.
-    auto start_unit = [&](const Cursor &u, bool with_new, u32x4 (&knew)[NL], u32x4 (&vnew)[NL]) {
+    auto load_q = [&](const Cursor &u, u32x4 (&qd)[NL]) __attribute__((always_inline)) {
         const char *qb = static_cast<const char *>(a.q) + uniform(((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW);
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, G * ROW, kBufferFlags);
         const int qoff = c * ROW + 16 * rg;  // head c (out of range, so zero, for c >= G)
-        static_for<0, NL>([&]<int b>() { qr[b] = load_chunk(rq, qoff + 64 * b); });
-        if (with_new) {
-            // the new token as a one-row tile in the K and V layouts
-            const int64_t nb = uniform(((int64_t)u.seq * Hkv + u.kvh) * ROW);
-            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(static_cast<const char *>(a.k_new) + nb), 0, ROW, kBufferFlags);
-            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(static_cast<const char *>(a.v_new) + nb), 0, ROW, kBufferFlags);
-            static_for<0, NL>([&]<int b>() { knew[b] = load_chunk(rk, koff + 64 * b); });
-            static_for<0, NL>([&]<int m>() { vnew[m] = load_chunk(rv, voff + 256 * m); });
-        }
-        // wait for q here, so that the sub-tile loop is entered with nothing
-        // but its own loads in flight and its waits stay exact
-#pragma unroll
-        for (int b = 0; b < NL; ++b) asm volatile("" ::"v"(qr[b]));
+        static_for<0, NL>([&]<int b>() { qd[b] = load_chunk(rq, qoff + 64 * b); });
+    };
+    auto reset_state = [&]() {
         m_run = kNegInf;
         l_run = 0.f;
         static_for<0, G>([&]<int h>() {
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
 
     // Merges the four row-group streams of (m, l, acc); afterwards every lane
     // holds the totals: m, l for head (lane % 16), acc for its chunks.
-    auto combine_rows = [&](float &m, float &l, float (&ac)[G][NCH][VEC], bool fold_half_rows) {
+    auto combine_rows = [&](float &m, float &l, float (&ac)[G][NCH][VEC], bool fold_half_rows) __attribute__((always_inline)) {
         float M = fmaxf(m, xor16(m));
         M = fmaxf(M, xor32(M, lane));
         const float Mu = M == kNegInf ? 0.f : M;
@@ -361,26 +362,18 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
                 float f[VEC];
                 static_for<0, VEC>([&]<int e>() { f[e] = ac[h][ch][e] * inv; });
                 const u32x4 pk = pack_chunk<DT>(f);
-                if (chunk_writer) *reinterpret_cast<u32x4 *>(ob + h * ROW + chunk_of(ch) * 16) = pk;
+                if (chunk_writer) store_chunk(ob, G * ROW, h * ROW + chunk_of(ch) * 16, pk);
             });
         });
     };
 
-    // Leaves the unit at `u` after sub-tile `g_last`: finish it here, or hand
-    // a partial result on and merge if this wave is the last to arrive.
     // ---- partial results: records of (max, exp-sum, acc) per query head.
     // A record holds acc[G][D] (fp32, relative to its max) and (max, exp-sum)[G].
     constexpr int kRecAcc = G * D * 4;   // bytes of a record's acc
     constexpr int NF = G * D / 4;        // float4 chunks of a record's acc
     constexpr int CPL = (NF + kWave - 1) / kWave;  // chunks per lane in the flat layout
-    auto arrive = [&](int32_t *ctr) {
-        wait_vmem_done();  // this wave's record stores are complete before it counts itself
-        int old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return __builtin_amdgcn_readlane(old, 0);
-    };
     auto reset = [&](int32_t *ctr) {
-        if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) store_counter(ctr, 0);
     };
     // Merges records [first, first + cnt) of a record array into the flat
     // layout (lane holds float4 chunks lane, lane + 64, ...): returns the
@@ -470,14 +463,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         });
         static_for<0, G>([&]<int h>() {
             if (lane == 0) {
-                __hip_atomic_store(rml + slot * G * 2 + 2 * h, Mh[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(rml + slot * G * 2 + 2 * h + 1, Lh[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                store_coherent_f32(rml + slot * G * 2, G * 8, 8 * h, Mh[h]);
+                store_coherent_f32(rml + slot * G * 2, G * 8, 8 * h + 4, Lh[h]);
             }
         });
     };
     // Writes a merged result in the flat layout as the unit's output.
-    auto write_out_flat = [&](const Cursor &u, const float (&Lh)[G], const f32x4 (&fa)[CPL]) {
-        char *ob = static_cast<char *>(a.out) + ((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW;
+    // Writes a merged result in the flat layout as the output of `unit`
+    // (its G query heads are rows unit * G .. unit * G + G - 1 of the output).
+    auto write_out_flat = [&](int unit, const float (&Lh)[G], const f32x4 (&fa)[CPL]) {
+        char *ob = static_cast<char *>(a.out) + (int64_t)unit * G * ROW;
         static_for<0, CPL>([&]<int j>() {
             const int q = j * kWave + lane;
             if (q < NF) {
@@ -499,76 +494,101 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         });
     };
 
-    // Leaves the unit at `u` after sub-tile `g_last`: finish it here, or hand
-    // a partial result on.  Partial results of a unit shared by k waves are
-    // merged in a two-level tree: groups of about sqrt(k) consecutive segments
-    // are merged by the last of their waves to arrive, then the group results
-    // by the last group to arrive, so that no wave reads more than about
-    // sqrt(k) records (k is known statically from the split).
-    auto finish_unit = [&](const Cursor &u, int g_last) {
-        combine_rows(m_run, l_run, acc, true);
-        const int ua = Hkv * u.pre + u.kvh * u.n;  // unit's first sub-tile
-        const int ub = ua + u.n;
-        if (seg_first == ua && g_last + 1 == ub) {  // the whole unit was ours
-            write_out(u, acc, l_run);
-            return;
-        }
+    // ---- a unit shared by k waves leaves k partial records, merged in a
+    // two-level tree: groups of about sqrt(k) consecutive segments are merged
+    // by the last of their waves to arrive, then the group results by the last
+    // group to arrive, so that no wave reads more than about sqrt(k) records
+    // (k is known statically from the split).  The record slots of a unit are
+    // base .. base + k - 1 with base = w_first + unit.
+    struct Split {
+        int unit;     // (sequence, KV head) index
+        int k;        // waves that share the unit
+        int wfirst;   // the first of them
+    };
+    struct Tree {
+        int f1, ng, j, kj;   // group size, groups, this wave's group and its size
+    };
+    auto split_of = [&](const Cursor &u) -> Split {
         // augmented position of the unit's first sub-tile, past its ghosts
         const int64_t xa = ((int64_t)u.pre + (int64_t)C * u.cnt) * Hkv + (int64_t)u.kvh * (u.n + C) + C;
-        const int w_first = wave_of(xa);
-        const int w_last = wave_of(xa + u.n - 1);
-        const int k = w_last - w_first + 1;
-        const int unit = u.seq * Hkv + u.kvh;
-        const int64_t base = (int64_t)w_first + unit;  // slots of this unit: base .. base + k - 1
-        // this segment's record
-        const int64_t slot = (int64_t)wave + unit;
-        {
-            float *pacc = a.ws_acc + slot * G * D;
-            float *pml = a.ws_ml + slot * G * 2;
-            static_for<0, G>([&]<int h>() {
-                static_for<0, NCH>([&]<int ch>() {
-                    if (chunk_writer) {
-                        static_for<0, VEC / 4>([&]<int v4>() {
-                            const f32x4 x = {acc[h][ch][4 * v4], acc[h][ch][4 * v4 + 1], acc[h][ch][4 * v4 + 2],
-                                             acc[h][ch][4 * v4 + 3]};
-                            store_coherent(pacc, kRecAcc, (h * D + chunk_of(ch) * VEC + 4 * v4) * 4, x);
-                        });
-                    }
-                });
+        Split s;
+        s.wfirst = wave_of(xa);
+        s.k = wave_of(xa + u.n - 1) - s.wfirst + 1;
+        s.unit = unit_of(u);
+        return s;
+    };
+    auto tree_of = [&](const Split &s) -> Tree {
+        Tree tr;
+        int f1 = (int)__builtin_sqrtf((float)s.k);
+        while (f1 * f1 < s.k) ++f1;
+        tr.f1 = f1;
+        tr.ng = (s.k + f1 - 1) / f1;
+        tr.j = (wave - s.wfirst) / f1;
+        tr.kj = min(f1, s.k - tr.j * f1);
+        return tr;
+    };
+    // this segment's record
+    auto store_record = [&](const Split &s) __attribute__((always_inline)) {
+        const int64_t slot = (int64_t)wave + s.unit;
+        float *pacc = a.ws_acc + slot * G * D;
+        float *pml = a.ws_ml + slot * G * 2;
+        static_for<0, G>([&]<int h>() {
+            static_for<0, NCH>([&]<int ch>() {
+                if (chunk_writer) {
+                    static_for<0, VEC / 4>([&]<int v4>() {
+                        const f32x4 x = {acc[h][ch][4 * v4], acc[h][ch][4 * v4 + 1], acc[h][ch][4 * v4 + 2],
+                                         acc[h][ch][4 * v4 + 3]};
+                        store_coherent(pacc, kRecAcc, (h * D + chunk_of(ch) * VEC + 4 * v4) * 4, x);
+                    });
+                }
             });
-            if (rg == 0 && c < G) {
-                __hip_atomic_store(pml + 2 * c, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(pml + 2 * c + 1, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+        });
+        if (rg == 0 && c < G) {
+            store_coherent_f32(pml, G * 8, 8 * c, m_run);
+            store_coherent_f32(pml, G * 8, 8 * c + 4, l_run);
         }
+    };
+    // The arrival of a segment: a relaxed agent-scope add on the unit's (or
+    // its group's) counter, issued only once the segment's record stores have
+    // completed.  The returned count (in lane 0) is read later.
+    auto post_arrival = [&](const Split &s) -> int {
+        int32_t *ctr = a.ws_cnt + s.unit;
+        if (s.k > kDirectMerge) ctr = a.ws_gcnt + ((int64_t)s.wfirst + s.unit + tree_of(s).j);
+        int old = 0;
+        if (lane == 0) old = atomic_add_counter(ctr, 1);
+        return old;
+    };
+    // After the arrival returned the count `got`: merges and writes the
+    // output if this wave was the last of the unit (or of its group, then of
+    // the groups).
+    auto complete = [&](const Split &s, int got) {
         float Mh[G], Lh[G];
         f32x4 fa[CPL];
-        if (k <= kDirectMerge) {
-            if (arrive(a.ws_cnt + unit) != k - 1) return;
-            merge_flat(a.ws_acc, a.ws_ml, base, k, Mh, Lh, fa);
-            write_out_flat(u, Lh, fa);
-            reset(a.ws_cnt + unit);
+        const int64_t base = (int64_t)s.wfirst + s.unit;
+        if (s.k <= kDirectMerge) {
+            if (got != s.k - 1) return;
+            merge_flat(a.ws_acc, a.ws_ml, base, s.k, Mh, Lh, fa);
+            write_out_flat(s.unit, Lh, fa);
+            reset(a.ws_cnt + s.unit);
             return;
         }
-        int f1 = (int)__builtin_sqrtf((float)k);
-        while (f1 * f1 < k) ++f1;
-        const int ng = (k + f1 - 1) / f1;
-        const int r = wave - w_first;
-        const int j = r / f1;
-        const int kj = min(f1, k - j * f1);
-        const int64_t gslot = base + j;
-        if (arrive(a.ws_gcnt + gslot) != kj - 1) return;
-        merge_flat(a.ws_acc, a.ws_ml, base + (int64_t)j * f1, kj, Mh, Lh, fa);
+        const Tree tr = tree_of(s);
+        if (got != tr.kj - 1) return;
+        const int64_t gslot = base + tr.j;
+        merge_flat(a.ws_acc, a.ws_ml, base + (int64_t)tr.j * tr.f1, tr.kj, Mh, Lh, fa);
         store_flat_record(a.ws_gacc, a.ws_gml, gslot, Mh, Lh, fa);
         reset(a.ws_gcnt + gslot);
-        if (arrive(a.ws_cnt + unit) != ng - 1) return;
-        merge_flat(a.ws_gacc, a.ws_gml, base, ng, Mh, Lh, fa);
-        write_out_flat(u, Lh, fa);
-        reset(a.ws_cnt + unit);
+        wait_vmem_done();
+        int og = 0;
+        if (lane == 0) og = atomic_add_counter(a.ws_cnt + s.unit, 1);
+        if (__builtin_amdgcn_readlane(og, 0) != tr.ng - 1) return;
+        merge_flat(a.ws_gacc, a.ws_gml, base, tr.ng, Mh, Lh, fa);
+        write_out_flat(s.unit, Lh, fa);
+        reset(a.ws_cnt + s.unit);
     };
 
     // One sub-tile: scores on MFMA, four-stream online softmax, acc += p V.
-    auto process_rows = [&](int nvalid, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) {
+    auto process_rows = [&](int nvalid, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) __attribute__((always_inline)) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
         static_for<0, NL>([&]<int b>() { s = mfma_chunk<DT>(kr[b], qr[b], s); });
         float sv[4];
@@ -605,35 +625,68 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             });
         });
     };
-    auto process = [&](const Cursor &u, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) {
-        process_rows(u.L - (u.sub << 4), kr, vr);  // valid rows: >= 1
-    };
-    // Fused step, unit's first sub-tile: fold the appended token (position
-    // L - 1 of the sequence) into the running state and store it in its slot.
-    auto fold_new_token = [&](const Cursor &u, const u32x4 (&knew)[NL], const u32x4 (&vnew)[NL]) {
-        process_rows(1, knew, vnew);
-        const int64_t so = uniform(slot_offset(u.seq, u.kvh, u.L));
+    // The sub-tile at `u`; in a fused step the unit's last one also stores
+    // the appended token into its slot, from the lanes that hold its row.
+    auto process = [&](const Cursor &u, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) __attribute__((always_inline)) {
+        if (!holds_new(u)) {
+            process_rows(u.L - (u.sub << 4), kr, vr);  // valid rows: >= 1
+            return;
+        }
+        u32x4 k2[NL], v2[NL];
+        static_for<0, NL>([&]<int b>() { k2[b] = kr[b] | knew[b]; v2[b] = vr[b] | vnew[b]; });
+        process_rows(u.L - (u.sub << 4), k2, v2);
+        const int rn = u.L - 1 - (u.sub << 4);
+        const int64_t so = tile_offset(u) + (int64_t)rn * ROW;
         char *kd = static_cast<char *>(a.k_cache_w) + so;
         char *vd = static_cast<char *>(a.v_cache_w) + so;
         static_for<0, NL>([&]<int b>() {
-            if (koff + 64 * b < ROW) *reinterpret_cast<u32x4 *>(kd + koff + 64 * b) = knew[b];
+            if (c == rn) store_chunk(kd, ROW, 16 * rg + 64 * b, knew[b]);
         });
         static_for<0, NL>([&]<int m>() {
-            if (voff + 256 * m < ROW) *reinterpret_cast<u32x4 *>(vd + voff + 256 * m) = vnew[m];
+            const int o = voff + 256 * m;
+            if (o / ROW == rn) store_chunk(vd, ROW, o - rn * ROW, vnew[m]);
         });
     };
+    // Requests the q of the unit after the one `u` ends, when `u` (sub-tile
+    // gidx) is its unit's last, that unit lies in this range and no earlier
+    // request is still waiting to be taken over.
+    auto prefetch_q = [&](const Cursor &u, int gidx) __attribute__((always_inline)) {
+        if (u.sub + 1 == u.n && gidx + 1 < g1 && qn_unit < 0) {
+            Cursor nx = u;
+            advance(nx);
+            load_q(nx, qn);
+            qn_unit = unit_of(nx);
+        }
+    };
+    // Loads that depend on what the sub-tile just issued at `u` is: the
+    // appended token's row and the next unit's q.  They are issued after the
+    // step's compute rather than with the sub-tile's loads, so that the wait of
+    // that compute (whose count the compiler takes over both paths) does not
+    // include them.
+    auto issue_extras = [&](const Cursor &u, int gidx) __attribute__((always_inline)) {
+        if (holds_new(u)) issue_new(u);
+        prefetch_q(u, gidx);
+    };
 
-    // ---- main loop over [g0, g1): one outer iteration per segment (the part
-    // of a unit inside this range).  kDepth sub-tiles are in flight: the inner
-    // loop issues the loads of sub-tile g + kDepth - 1 before it consumes
-    // sub-tile g, unconditionally (empty ranges past the end), so its waits
-    // only ever cover the sub-tile being consumed.  The first sub-tiles of the
-    // next segment are already in flight when a segment ends.
+    // ---- main loop over [g0, g1), kDepth sub-tiles in flight: each step
+    // issues the loads of sub-tile gl + 1 and then consumes sub-tile g,
+    // unconditionally (empty ranges past the end), so its waits only ever
+    // cover the sub-tile being consumed.  The step is unrolled kDepth times so
+    // that the buffers rotate without moves.  A segment (the part of a unit
+    // inside the range) that ends before the range does is finished in the
+    // loop: a whole unit writes its output; the range's first segment, when
+    // its unit began in an earlier range, writes a partial record and reports
+    // its arrival a few sub-tiles later, once the record's stores are known to
+    // be complete (vector memory accesses complete in issue order, and loads
+    // issued after the stores have then returned).  The range's last segment
+    // is finished after the loop, where any merge this wave owes happens.
     u32x4 kbuf[kDepth][NL], vbuf[kDepth][NL];
-    Cursor cp = cur;   // the sub-tile being consumed (g), in buffer 0 at a segment start
+    Cursor cp = cur;   // the sub-tile being consumed (g)
     Cursor cl = cur;   // the most recently issued sub-tile ...
     int gl = g0;       // ... and its index
+    load_q(cur, qr);
     issue(cl, true, kbuf[0], vbuf[0]);
+    issue_extras(cl, gl);
     static_for<1, kDepth - 1>([&]<int m>() {
         const bool more = gl + 1 < g1;
         if (more) {
@@ -641,64 +694,98 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             ++gl;
         }
         issue(cl, more, kbuf[m], vbuf[m]);
+        if (more) issue_extras(cl, gl);
     });
+    reset_state();
     int g = g0;
-    while (true) {
-        if (fused && cp.sub == 0) {
-            u32x4 knew[NL], vnew[NL];
-            start_unit(cp, true, knew, vnew);
-            fold_new_token(cp, knew, vnew);
-        } else {
-            u32x4 knew[NL], vnew[NL];   // unused
-            start_unit(cp, false, knew, vnew);
-        }
-        seg_first = g;
-        int brk = 0;
-        bool done = false;
-        while (!done) {
-            static_for<0, kDepth>([&]<int i>() {
-                if (done) return;
-                constexpr int nb = (i + kDepth - 1) % kDepth;
-                const bool more = gl + 1 < g1;
-                if (more) {
-                    advance(cl);
-                    ++gl;
-                }
-                issue(cl, more, kbuf[nb], vbuf[nb]);
-                process(cp, kbuf[i], vbuf[i]);
-                if (cp.sub + 1 == cp.n || g + 1 == g1) {
-                    brk = i;
-                    done = true;
-                    return;
+    int seg_first = g0;
+    bool pend = false;      // the range's first segment left a record ...
+    int arrive_at = -1;     // ... whose arrival is posted once sub-tile arrive_at is consumed
+    int pend_old = 0;       // the count it returned (lane 0)
+    Split psplit{};
+    bool stop = false;
+    while (!stop) {
+        static_for<0, kDepth>([&]<int i>() {
+            if (stop) return;
+            constexpr int nb = (i + kDepth - 1) % kDepth;
+            const bool more = gl + 1 < g1;
+            if (more) {
+                advance(cl);
+                ++gl;
+            }
+            issue(cl, more, kbuf[nb], vbuf[nb]);
+            process(cp, kbuf[i], vbuf[i]);
+            if (g == arrive_at) {
+                // The loads of this sub-tile were issued after the record's
+                // stores and have been consumed, and vector memory accesses
+                // complete in issue order: the stores are complete.  The
+                // arrival's count is read at the end of the range.
+                asm volatile("" ::"v"(acc[0][0][0]), "v"(l_run) : "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                pend_old = post_arrival(psplit);
+                arrive_at = -1;
+            }
+            if (g + 1 == g1) {
+                stop = true;
+                return;
+            }
+            if (cp.sub + 1 == cp.n) {
+                // a segment ends inside the range
+                combine_rows(m_run, l_run, acc, true);
+                const int ua = Hkv * cp.pre + cp.kvh * cp.n;
+                if (seg_first == ua) {
+                    write_out(cp, acc, l_run);
+                } else {
+                    psplit = split_of(cp);
+                    store_record(psplit);
+                    // keep the record's stores ahead of the next sub-tile's loads
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+                    pend = true;
+                    arrive_at = gl + 1;
                 }
                 advance(cp);
                 ++g;
-            });
-        }
-        finish_unit(cp, g);
-        if (g + 1 >= g1) break;
-        advance(cp);
-        ++g;
-        // the next sub-tile sits in buffer brk + 1: rotate it to buffer 0
-        static_for<0, kDepth - 1>([&]<int b>() {
-            if (brk == b) {
-                u32x4 tk[kDepth][NL], tv[kDepth][NL];
-                static_for<0, kDepth>([&]<int m>() {
-                    static_for<0, NL>([&]<int e>() { tk[m][e] = kbuf[m][e]; tv[m][e] = vbuf[m][e]; });
-                });
-                static_for<0, kDepth - 1>([&]<int m>() {
-                    constexpr int from = (b + 1 + m) % kDepth;
-                    static_for<0, NL>([&]<int e>() { kbuf[m][e] = tk[from][e]; vbuf[m][e] = tv[from][e]; });
-                });
+                seg_first = g;
+                if (qn_unit == unit_of(cp)) {
+                    static_for<0, NL>([&]<int b>() { qr[b] = qn[b]; });
+                    qn_unit = -1;
+                } else {
+                    load_q(cp, qr);
+                }
+                reset_state();
+            } else {
+                advance(cp);
+                ++g;
             }
+            if (more) issue_extras(cl, gl);
         });
     }
+
+    // ---- the range's last segment (sub-tile g1 - 1 was the last consumed)
+    combine_rows(m_run, l_run, acc, true);
+    const int ua_last = Hkv * cp.pre + cp.kvh * cp.n;
+    const bool last_whole = seg_first == ua_last && g + 1 == ua_last + cp.n;
+    Split lsplit{};
+    if (last_whole) {
+        write_out(cp, acc, l_run);
+    } else {
+        lsplit = split_of(cp);
+        store_record(lsplit);
+    }
+    if (last_whole && !pend) return;
+    wait_vmem_done();   // the records' stores are complete
+    int last_old = 0;
+    if (!last_whole) last_old = post_arrival(lsplit);
+    if (pend && arrive_at >= 0) pend_old = post_arrival(psplit);
+    if (!last_whole) complete(lsplit, __builtin_amdgcn_readlane(last_old, 0));
+    if (pend) complete(psplit, __builtin_amdgcn_readlane(pend_old, 0));
 }
 
 template <typename DT, int D, int G>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.num_waves / kWavesPerGroup));
-    attn_stream_kernel<DT, D, G><<<grid, dim3(kWavesPerGroup * kWave), 0, stream>>>(a);
+    attn_stream_kernel<DT, D, G><<<grid, dim3(kWavesPerGroup * kWave), kDecodeLdsPin, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -706,7 +793,7 @@ template <typename DT, int D, int G>
 int waves_per_cu_typed() {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_stream_kernel<DT, D, G>,
-                                                     kWavesPerGroup * kWave, 0) != hipSuccess)
+                                                     kWavesPerGroup * kWave, kDecodeLdsPin) != hipSuccess)
         return 0;
     return blocks * kWavesPerGroup;
 }

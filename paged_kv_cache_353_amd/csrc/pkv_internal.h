@@ -77,7 +77,13 @@ hipError_t launch_check(const CheckArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode
 constexpr int kWavesPerGroup = 4;   // independent waves per workgroup
-constexpr int kWavesPerSimd = 2;    // resident waves per SIMD the grid is sized for (at most)
+constexpr int kWavesPerSimd = 1;    // resident waves per SIMD the grid is sized for (at most)
+// Dynamic LDS reserved (and not used) by each one-query decode workgroup, so
+// that a CU (160 KiB of LDS) holds one of them: four waves, one per SIMD.
+// The kernel's registers would let two share a SIMD, and then the older wave
+// of each SIMD takes the memory pipeline while the younger one's equal share
+// finishes long after it.
+constexpr unsigned kDecodeLdsPin = 96u * 1024u;
 constexpr int kMaxWaves = 8192;     // 256 CUs x 32 resident waves; sizes the workspace
 // Arrival counters sit in a region of fixed size at the start of every
 // workspace, so that partial results written by a call of one shape never
