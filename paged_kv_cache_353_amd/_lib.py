@@ -108,6 +108,45 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _require_device(device: torch.device, **tensors) -> None:
+    """Every tensor must live on ``device`` (a GPU): the library is handed raw
+    pointers, and a host pointer would reach a kernel as a device address."""
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+# Zeroed workspaces kept per (device, stream) for calls that pass none: the
+# arrival counters at the start of a workspace are returned to zero by every
+# call, so one buffer serves every later call on the same stream.  Calls on
+# other streams get their own, since calls that may overlap must not share one.
+_ws_lock = threading.Lock()
+_ws_cache = {}
+
+
+def _default_workspace(device: torch.device, need: int) -> torch.Tensor:
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    with _ws_lock:
+        ws = _ws_cache.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
+            _ws_cache[key] = ws
+        return ws
+
+
+def _check_workspace(workspace: Optional[torch.Tensor], device: torch.device, need: int) -> torch.Tensor:
+    if workspace is None:
+        return _default_workspace(device, need)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    _require_device(device, workspace=workspace)
+    return workspace
+
+
 class _on_device:
     """Makes ``device`` current for the duration of a call (the library
     launches on the current HIP device), skipping the switch when it already
@@ -150,6 +189,7 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
             raise ValueError("k/v rows must be contiguous within a token")
     if not (k_cache.is_contiguous() and v_cache.is_contiguous() and slot_mapping.is_contiguous()):
         raise ValueError("caches and slot_mapping must be contiguous")
+    _require_device(k_cache.device, k=k, v=v, v_cache=v_cache, slot_mapping=slot_mapping)
     nb, hkv, bs, d = k_cache.shape
     lib = load_library()
     with _on_device(k_cache.device):
@@ -169,6 +209,7 @@ def paged_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
         raise ValueError("block_pairs must be int64 [num_pairs, 2]")
     if not (k_cache.is_contiguous() and v_cache.is_contiguous() and block_pairs.is_contiguous()):
         raise ValueError("caches and block_pairs must be contiguous")
+    _require_device(k_cache.device, v_cache=v_cache, block_pairs=block_pairs)
     nb, hkv, bs, d = k_cache.shape
     lib = load_library()
     with _on_device(k_cache.device):
@@ -195,6 +236,7 @@ def paged_check_inputs(block_tables: torch.Tensor, context_lens: torch.Tensor, n
     if not (block_tables.is_contiguous() and context_lens.is_contiguous()):
         raise ValueError("block_tables and context_lens must be contiguous")
     dev = block_tables.device
+    _require_device(dev, context_lens=context_lens, slot_mapping=slot_mapping)
     ntok, sptr = 0, None
     if slot_mapping is not None:
         if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or not slot_mapping.is_contiguous():
@@ -238,6 +280,8 @@ def _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, blo
             raise ValueError("all tensors must be contiguous")
     if int(block_size) != k_cache.shape[2]:
         raise ValueError("block_size must equal k_cache.shape[2]")
+    _require_device(q.device, out=out, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                    context_lens=context_lens)
 
 
 def paged_decode_step(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -258,13 +302,13 @@ def paged_decode_step(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v
         raise TypeError("k_new/v_new must have the caches' dtype")
     if not (k_new.is_contiguous() and v_new.is_contiguous()):
         raise ValueError("k_new and v_new must be contiguous")
+    _require_device(q.device, k_new=k_new, v_new=v_new)
     mb = block_tables.shape[1]
     if max_context_len is None:
         max_context_len = mb * bs
     lib = load_library()
     need = int(lib.paged_attn_decode_workspace_size(S, hq, hkv, d, bs, int(max_context_len)))
-    if workspace is None:
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _check_workspace(workspace, q.device, need)
     with _on_device(q.device):
         _check(lib.paged_decode_step(
             out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
@@ -292,8 +336,9 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     arrival counters in its first 8,421,376 bytes.  A caller-provided workspace
     must have that region zero-filled once before its first use; every call
     returns the counters to zero, so it can be reused by later calls on the
-    same stream (not by calls that run concurrently).  When not given, a zeroed one is allocated through
-    torch.  Returns ``out``.
+    same stream (not by calls that run concurrently).  When not given, the
+    binding keeps one zeroed workspace per (device, stream) and reuses it,
+    growing it when a call needs more.  Returns ``out``.
     """
     _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, block_size)
     S, hq, d = q.shape
@@ -303,8 +348,7 @@ def paged_attn_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
         max_context_len = mb * bs
     lib = load_library()
     need = int(lib.paged_attn_decode_workspace_size(S, hq, hkv, d, bs, int(max_context_len)))
-    if workspace is None:
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _check_workspace(workspace, q.device, need)
     with _on_device(q.device):
         _check(lib.paged_attn_decode(
             out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -329,6 +373,7 @@ def _check_cache_args(k_cache, v_cache, block_tables, context_lens, num_seqs, dt
             raise ValueError("all tensors must be contiguous")
     if int(block_size) != k_cache.shape[2]:
         raise ValueError("block_size must equal k_cache.shape[2]")
+    _require_device(k_cache.device, v_cache=v_cache, block_tables=block_tables, context_lens=context_lens)
 
 
 def paged_attn_decode_multi_workspace_size(num_seqs: int, num_query_tokens: int, num_q_heads: int,
@@ -354,14 +399,14 @@ def paged_attn_decode_multi(out: torch.Tensor, q: torch.Tensor, k_cache: torch.T
         raise ValueError("all tensors must be contiguous")
     S, T, hq, d = q.shape
     _check_cache_args(k_cache, v_cache, block_tables, context_lens, S, q.dtype, block_size)
+    _require_device(k_cache.device, q=q, out=out)
     nb, hkv, bs, _ = k_cache.shape
     mb = block_tables.shape[1]
     if max_context_len is None:
         max_context_len = mb * bs
     lib = load_library()
     need = int(lib.paged_attn_decode_multi_workspace_size(S, T, hq, hkv, d))
-    if workspace is None:
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _check_workspace(workspace, q.device, need)
     with _on_device(q.device):
         _check(lib.paged_attn_decode_multi(
             out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -401,6 +446,7 @@ def paged_attn_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.
         raise ValueError("group_starts must be [num_groups + 1] and prefix_lens [num_seqs]")
     if not (group_starts.is_contiguous() and prefix_lens.is_contiguous()):
         raise ValueError("all tensors must be contiguous")
+    _require_device(q.device, group_starts=group_starts, prefix_lens=prefix_lens)
     ng = group_starts.shape[0] - 1
     nb, hkv, bs, _ = k_cache.shape
     mb = block_tables.shape[1]
@@ -408,8 +454,7 @@ def paged_attn_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.
         max_context_len = mb * bs
     lib = load_library()
     need = int(lib.paged_attn_decode_shared_workspace_size(S, ng, hq, hkv, d))
-    if workspace is None:
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _check_workspace(workspace, q.device, need)
     with _on_device(q.device):
         _check(lib.paged_attn_decode_shared(
             out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),

@@ -130,10 +130,13 @@ class BlockManager:
         """One new token for each sequence of ``sids``, in order.
 
         Returns the slot of every token (int64, the ``slot_mapping`` of the KV
-        write) and the (src, dst) block pairs to copy first (int64 [k, 2], the
+        write) and the (src, dst) block pairs to copy (int64 [k, 2], the
         argument of the device block copy).  Sources and destinations are
-        disjoint: a destination is freshly allocated, and a source keeps at
-        least one other reference, so it is never written in this batch.
+        disjoint (a destination is freshly allocated), but a source can be
+        written in the same batch: the last sequence still referencing it
+        appends in place, into the row just past the copied ones.  So the copies
+        must complete before the KV write of the batch: issue the block copy
+        first, on the same stream as the write.
         """
         slots = np.empty(len(sids), dtype=np.int64)
         pairs = []

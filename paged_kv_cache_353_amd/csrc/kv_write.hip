@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a, int chunks
     const int32_t h = rem / chunks_per_row;
     const int32_t c = rem - h * chunks_per_row;
     const int64_t slot = a.slot_mapping[n];
-    if (slot < 0) return;
+    if (slot < 0 || slot >= a.num_slots) return;   // skipped, or outside the pool
     const int64_t blk = slot / a.block_size;
     const int64_t off = slot - blk * a.block_size;
     const int64_t row_bytes = (int64_t)a.head_dim * a.elem_bytes;

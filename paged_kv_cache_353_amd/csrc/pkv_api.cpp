@@ -3,6 +3,7 @@
 // device memory or synchronises.
 #include "pkv.h"
 
+#include <atomic>
 #include <cmath>
 
 #include "pkv_internal.h"
@@ -23,6 +24,25 @@ int elem_bytes(int32_t dtype) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device, asked once per device: the attribute
+// query costs more than the launch it sizes.
+constexpr int kMaxDevices = 64;
+int current_device_cus(int *device_out) {
+    static std::atomic<int> cache[kMaxDevices];
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return 0;
+    if (device_out) *device_out = device;
+    if (device < 0 || device >= kMaxDevices) {
+        int cus = 0;
+        return hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess ? cus : 0;
+    }
+    int cus = cache[device].load(std::memory_order_relaxed);
+    if (cus > 0) return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 0;
+    cache[device].store(cus, std::memory_order_relaxed);
+    return cus;
+}
 
 }  // namespace
 
@@ -69,6 +89,7 @@ int paged_kv_write(const void *k, const void *v, void *k_cache, void *v_cache,
     a.v_cache = v_cache;
     a.slot_mapping = slot_mapping;
     a.num_tokens = num_tokens;
+    a.num_slots = num_blocks * (int64_t)block_size;
     a.k_token_stride = k_token_stride;
     a.v_token_stride = v_token_stride;
     a.num_kv_heads = num_kv_heads;
@@ -165,14 +186,23 @@ int decode_through_multi(void *out, const void *q, const void *k_new, const void
                          float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
-// Shared by paged_attn_decode (k_new == v_new == NULL) and paged_decode_step.
-int decode_impl(void *out, const void *q, const void *k_new, const void *v_new,
-                const void *k_cache, const void *v_cache, const int32_t *block_tables,
-                const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
-                float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
-                hipStream_t stream) {
+// Where a decode call keeps its arrival counters and partial records.
+struct DecodeScratch {
+    int32_t *cnt;
+    int32_t *gcnt;
+    float *acc;
+    float *ml;
+    float *gacc;
+    float *gml;
+};
+
+// Host checks of a one-query decode call; sets *one_query to whether the
+// one-query kernel serves it (the others go to the many-column kernel).
+int decode_checks(const void *out, const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                  const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                  int32_t max_context_len, float scale, int32_t dtype, bool *one_query) {
     if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
@@ -185,16 +215,11 @@ int decode_impl(void *out, const void *q, const void *k_new, const void *v_new,
     const int32_t group = num_q_heads / num_kv_heads;
     // The one-query kernel serves group sizes 1, 2, 4 and 8 where it keeps
     // its state in registers; other group sizes, and configurations whose
-    // compiled kernel spills (head_dim 128 with 8 query heads per KV head:
-    // about ten times slower), go to the many-column kernel.
-    const bool one_query = pkv::decode_supported(dtype, head_dim, group) && block_size % 16 == 0 &&
-                           block_size <= 256 &&
-                           !(num_seqs > 0 && pkv::decode_scratch_bytes(dtype, head_dim, group) > 0);
-    if (!one_query)
-        return decode_through_multi(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
-                                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                    max_blocks_per_seq, num_blocks, max_context_len, scale, dtype, workspace,
-                                    workspace_bytes, stream);
+    // compiled kernel spills (at present bf16 with 8 query heads per KV head;
+    // a spilling build ran about ten times slower), go to the many-column kernel.
+    *one_query = pkv::decode_supported(dtype, head_dim, group) && block_size % 16 == 0 && block_size <= 256 &&
+                 !(num_seqs > 0 && pkv::decode_scratch_bytes(dtype, head_dim, group) > 0);
+    if (!*one_query) return PKV_OK;
     // sub-tile indices of the whole batch are kept in 32 bits
     if ((int64_t)num_seqs * num_kv_heads * (((int64_t)max_context_len + 15) / 16) >= ((int64_t)1 << 31))
         return PKV_ERR_UNSUPPORTED;
@@ -204,23 +229,25 @@ int decode_impl(void *out, const void *q, const void *k_new, const void *v_new,
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_ERR_ALIGN;
     if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGN;
-    const pkv::DecodeWorkspace ws = pkv::decode_workspace(num_seqs, num_kv_heads, group, head_dim);
-    if (!workspace || workspace_bytes < ws.bytes) return PKV_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
+    return PKV_OK;
+}
 
-    // grid: as many waves as the GPU holds at once
-    int device = 0, cus = 0;
-    if (hipGetDevice(&device) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
-        return PKV_ERR_HIP;
+// Waves of the one-query decode grid: as many as the GPU holds at once (0 on error).
+int64_t decode_grid_waves(int32_t dtype, int32_t head_dim, int32_t group) {
+    const int cus = current_device_cus(nullptr);
     int per_cu = pkv::decode_waves_per_cu(dtype, head_dim, group);
-    if (per_cu <= 0 || cus <= 0) return PKV_ERR_HIP;
+    if (per_cu <= 0 || cus <= 0) return 0;
     per_cu = per_cu < 4 * pkv::kWavesPerSimd ? per_cu : 4 * pkv::kWavesPerSimd;
     int64_t waves = (int64_t)cus * per_cu;
     waves = waves < pkv::kMaxWaves ? waves : pkv::kMaxWaves;
-    waves -= waves % pkv::kWavesPerGroup;
+    return waves - waves % pkv::kWavesPerGroup;
+}
 
-    char *w = static_cast<char *>(workspace);
+int decode_launch(void *out, const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                  const void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                  int32_t dtype, int64_t waves, const DecodeScratch &s, hipStream_t stream) {
     pkv::DecodeArgs a{};
     a.out = out;
     a.q = q;
@@ -233,12 +260,12 @@ int decode_impl(void *out, const void *q, const void *k_new, const void *v_new,
     // the fused step writes the appended token into the caches it was given
     a.k_cache_w = const_cast<void *>(k_cache);
     a.v_cache_w = const_cast<void *>(v_cache);
-    a.ws_cnt = reinterpret_cast<int32_t *>(w + ws.cnt_offset);
-    a.ws_gcnt = reinterpret_cast<int32_t *>(w + ws.gcnt_offset);
-    a.ws_acc = reinterpret_cast<float *>(w + ws.acc_offset);
-    a.ws_ml = reinterpret_cast<float *>(w + ws.ml_offset);
-    a.ws_gacc = reinterpret_cast<float *>(w + ws.gacc_offset);
-    a.ws_gml = reinterpret_cast<float *>(w + ws.gml_offset);
+    a.ws_cnt = s.cnt;
+    a.ws_gcnt = s.gcnt;
+    a.ws_acc = s.acc;
+    a.ws_ml = s.ml;
+    a.ws_gacc = s.gacc;
+    a.ws_gml = s.gml;
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
@@ -247,9 +274,43 @@ int decode_impl(void *out, const void *q, const void *k_new, const void *v_new,
     a.max_context_len = max_context_len;
     a.num_waves = (int32_t)waves;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-    return pkv::launch_attn_decode(dtype, head_dim, group, a, stream) == hipSuccess
+    return pkv::launch_attn_decode(dtype, head_dim, num_q_heads / num_kv_heads, a, stream) == hipSuccess
                ? PKV_OK
                : PKV_ERR_HIP;
+}
+
+// Shared by paged_attn_decode (k_new == v_new == NULL) and paged_decode_step.
+int decode_impl(void *out, const void *q, const void *k_new, const void *v_new,
+                const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+    bool one_query = false;
+    int st = decode_checks(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                           num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                           max_context_len, scale, dtype, &one_query);
+    if (st != PKV_OK) return st;
+    if (!one_query)
+        return decode_through_multi(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    max_blocks_per_seq, num_blocks, max_context_len, scale, dtype, workspace,
+                                    workspace_bytes, stream);
+    if (num_seqs == 0) return PKV_OK;
+    const int32_t group = num_q_heads / num_kv_heads;
+    const pkv::DecodeWorkspace ws = pkv::decode_workspace(num_seqs, num_kv_heads, group, head_dim);
+    if (!workspace || workspace_bytes < ws.bytes) return PKV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKV_ERR_ALIGN;
+    const int64_t waves = decode_grid_waves(dtype, head_dim, group);
+    if (waves <= 0) return PKV_ERR_HIP;
+    char *w = static_cast<char *>(workspace);
+    const DecodeScratch s{reinterpret_cast<int32_t *>(w + ws.cnt_offset), reinterpret_cast<int32_t *>(w + ws.gcnt_offset),
+                          reinterpret_cast<float *>(w + ws.acc_offset), reinterpret_cast<float *>(w + ws.ml_offset),
+                          reinterpret_cast<float *>(w + ws.gacc_offset), reinterpret_cast<float *>(w + ws.gml_offset)};
+    return decode_launch(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len,
+                         scale, dtype, waves, s, stream);
 }
 
 // Units of the multi-query kernel for these sizes (an upper bound in the
@@ -306,10 +367,7 @@ int multi_checks(const void *out, const void *q, const void *k_cache, const void
 int32_t chunks_for(int64_t cols) { return cols > pkv::kMultiCols ? 2 : 1; }
 
 int multi_waves(int32_t dtype, int32_t head_dim, int32_t chunks, int64_t *waves) {
-    int device = 0, cus = 0;
-    if (hipGetDevice(&device) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
-        return PKV_ERR_HIP;
+    const int cus = current_device_cus(nullptr);
     int per_cu = pkv::multi_waves_per_cu(dtype, head_dim, chunks);
     if (per_cu <= 0 || cus <= 0) return PKV_ERR_HIP;
     per_cu = per_cu < 4 * pkv::kMultiWavesPerSimd ? per_cu : 4 * pkv::kMultiWavesPerSimd;

@@ -15,6 +15,7 @@ struct KvWriteArgs {
     void *v_cache;
     const int64_t *slot_mapping;
     int64_t num_tokens;
+    int64_t num_slots;       // num_blocks * block_size: slots at or past it are skipped
     int64_t k_token_stride;  // elements
     int64_t v_token_stride;  // elements
     int32_t num_kv_heads;

@@ -249,3 +249,56 @@ def test_check_inputs_rejects_bad_arguments_on_host(lib):
     assert chk(res=(1 << 12) + 4) == PKV_ERR_ALIGN
     assert chk(sm=(1 << 12) + 4) == PKV_ERR_ALIGN
     assert chk(bmb=124) == PKV_ERR_WORKSPACE             # 64 * 16 slots need 32 words
+
+
+# ---------------------------------------------------------------------------
+# the binding refuses host tensors before anything reaches the library
+# ---------------------------------------------------------------------------
+
+def _host_inputs():
+    import torch
+    S, Hq, Hkv, D, bs, nb = 2, 8, 2, 64, 16, 8
+    return dict(q=torch.zeros(S, Hq, D, dtype=torch.bfloat16), out=torch.zeros(S, Hq, D, dtype=torch.bfloat16),
+                k_cache=torch.zeros(nb, Hkv, bs, D, dtype=torch.bfloat16),
+                v_cache=torch.zeros(nb, Hkv, bs, D, dtype=torch.bfloat16),
+                block_tables=torch.zeros(S, 4, dtype=torch.int32), context_lens=torch.ones(S, dtype=torch.int32),
+                k_new=torch.zeros(S, Hkv, D, dtype=torch.bfloat16), v_new=torch.zeros(S, Hkv, D, dtype=torch.bfloat16),
+                slot_mapping=torch.zeros(S, dtype=torch.int64), bs=bs)
+
+
+@pytest.fixture
+def no_library(monkeypatch):
+    """Fails the test if a wrapper reaches for the library."""
+    def refuse():
+        raise AssertionError("the library was called with host tensors")
+    monkeypatch.setattr(_lib, "load_library", refuse)
+
+
+def test_host_tensors_are_refused(no_library):
+    import torch
+    t = _host_inputs()
+    calls = [
+        lambda: pkv.paged_kv_write(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"]),
+        lambda: pkv.paged_attn_decode(t["out"], t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                      t["context_lens"], t["bs"], 0.125),
+        lambda: pkv.paged_decode_step(t["out"], t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                      t["block_tables"], t["context_lens"], t["bs"], 0.125),
+        lambda: pkv.paged_copy_blocks(t["k_cache"], t["v_cache"], torch.zeros(1, 2, dtype=torch.int64)),
+        lambda: pkv.paged_attn_decode_multi(t["out"][:, None], t["q"][:, None], t["k_cache"], t["v_cache"],
+                                            t["block_tables"], t["context_lens"], t["bs"], 0.125),
+        lambda: pkv.paged_attn_decode_shared(t["out"], t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                             t["context_lens"], torch.tensor([0, 2], dtype=torch.int32),
+                                             torch.zeros(2, dtype=torch.int32), t["bs"], 0.125),
+        lambda: pkv.paged_check_inputs(t["block_tables"], t["context_lens"], 8, t["bs"], 64),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError):
+            call()
+
+
+def test_workspace_must_be_bytes(no_library, monkeypatch):
+    import torch
+    dev = torch.device("cuda", 0)
+    # the dtype check comes before any device check or library call
+    with pytest.raises(ValueError, match="uint8"):
+        _lib._check_workspace(torch.zeros(16, dtype=torch.float32), dev, 16)

@@ -124,3 +124,33 @@ def test_fork_many_and_batched_append():
     _, pairs2 = mgr.append_batch(sids)
     assert pairs2.shape == (0, 2)
     assert mgr.fork_many(root, 0) == []
+
+
+def test_batched_append_copies_must_precede_the_write():
+    """Two forks share a partial block: the first to append copies it, the
+    second then owns the source and appends in place.  Each fork reads its own
+    token only when the block copy runs before the KV write."""
+    import oracle
+    bs, nb, H, D = 4, 8, 1, 2
+    pool = BlockPool(nb, order=np.arange(nb))
+    mgr = BlockManager(pool, block_size=bs)
+    s = mgr.new_sequence()
+    for _ in range(2):                      # half a block
+        mgr.append_token(s)
+    f = mgr.fork(s)
+    slots, pairs = mgr.append_batch([s, f])
+    assert pairs.tolist() == [[0, 1]]       # s copies block 0 into block 1 ...
+    assert slots.tolist() == [6, 2]         # ... and f appends into block 0, the source
+    # cache holding the two shared tokens (values 10, 11), the new tokens 100 (s), 200 (f)
+    k = np.zeros((nb, H, bs, D), dtype=np.float32)
+    k[0, 0, 0], k[0, 0, 1] = 10.0, 11.0
+    new = np.array([[[100.0, 100.0]], [[200.0, 200.0]]], dtype=np.float32)
+    kc, _ = oracle.copy_blocks(k, k, pairs)              # copy first ...
+    kc, _ = oracle.paged_kv_write(new, new, kc, kc, slots)  # ... then write
+    row = lambda c, sid, t: c[mgr.seqs[sid].table[t // bs], 0, t % bs, 0]
+    assert [row(kc, s, t) for t in range(3)] == [10.0, 11.0, 100.0]
+    assert [row(kc, f, t) for t in range(3)] == [10.0, 11.0, 200.0]
+    # the other order lets the copy carry f's token over s's
+    kw, _ = oracle.paged_kv_write(new, new, k, k, slots)
+    kw, _ = oracle.copy_blocks(kw, kw, pairs)
+    assert row(kw, s, 2) == 200.0
