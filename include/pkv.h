@@ -202,6 +202,36 @@ int paged_decode_step(void *out, const void *q, const void *k_new, const void *v
                       hipStream_t stream);
 
 /*
+ * paged_decode_step_static -- paged_decode_step for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid hipMalloc.  It takes no workspace and calls no allocator; its
+ * arrival counters and partial results live in a fixed device array of
+ * 24 MiB per GPU that the library holds until the process ends.  The first
+ * call on a device (with that device current, not under stream capture)
+ * looks the array up and clears its counters on the given stream; every call
+ * leaves them zero.  Every call on one GPU shares that array: calls that may
+ * overlap on one GPU (two streams, two threads) race and give wrong results.
+ *
+ * Arguments, preconditions and results are those of paged_decode_step (both
+ * run the same kernel and give bitwise equal outputs and caches), with these
+ * limits:
+ *   num_seqs * num_kv_heads <= 16384, and the partial results of that many
+ *   units plus one per wave of the grid fit the array
+ *   (about (1024 + units) * group * head_dim * 8 bytes)  -> PKV_ERR_WORKSPACE
+ *   configurations that paged_decode_step serves with its many-column kernel
+ *   (group sizes other than 1, 2, 4, 8, and those whose one-query kernel
+ *   would spill registers: at present bf16 with group 8)
+ *                                                       -> PKV_ERR_UNSUPPORTED
+ *   first call on a device under stream capture         -> PKV_ERR_HIP
+ */
+int paged_decode_step_static(void *out, const void *q, const void *k_new, const void *v_new,
+                             void *k_cache, void *v_cache, const int32_t *block_tables,
+                             const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                             float scale, int32_t dtype, hipStream_t stream);
+
+/*
  * paged_attn_decode_multi -- several query tokens per sequence.
  *
  * Parallel sampling, beam search and the verification of drafted tokens give

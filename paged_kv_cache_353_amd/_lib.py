@@ -70,6 +70,10 @@ def load_library() -> ctypes.CDLL:
                                           c_i32, c_i32, c_i32, c_i32, c_i64, c_i32, c_f, c_i32,
                                           c_p, c_sz, c_p]
         lib.paged_decode_step.restype = c_int
+        lib.paged_decode_step_static.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32,
+                                                 c_i32, c_i32, c_i32, c_i32, c_i64, c_i32, c_f, c_i32,
+                                                 c_p]
+        lib.paged_decode_step_static.restype = c_int
         lib.paged_copy_blocks.argtypes = [c_p, c_p, c_p, c_i64, c_i32, c_i32, c_i32, c_i64, c_i32, c_p]
         lib.paged_copy_blocks.restype = c_int
         lib.paged_attn_decode_multi_workspace_size.argtypes = [c_i32] * 5
@@ -315,6 +319,39 @@ def paged_decode_step(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v
             v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, hq, hkv, d,
             bs, mb, nb, int(max_context_len), float(scale), _dtype_code(q),
             workspace.data_ptr() if workspace.numel() else None, workspace.numel(),
+            _stream_handle(q.device)))
+    return out
+
+
+def paged_decode_step_static(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                             v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int,
+                             scale: float, max_context_len: Optional[int] = None) -> torch.Tensor:
+    """``paged_decode_step`` without a workspace: the library keeps its
+    counters and partial results in a fixed array on each GPU, so the call
+    allocates nothing.  Calls that overlap on one GPU share that array and race.
+    Sizes beyond its limits raise (``PKV_ERR_WORKSPACE``), as do the group sizes
+    and head sizes the one-query kernel does not serve (``PKV_ERR_UNSUPPORTED``).
+    Returns ``out``."""
+    _check_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, block_size)
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    if k_new.shape != (S, hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise TypeError("k_new/v_new must have the caches' dtype")
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("k_new and v_new must be contiguous")
+    _require_device(q.device, k_new=k_new, v_new=v_new)
+    mb = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mb * bs
+    lib = load_library()
+    with _on_device(q.device):
+        _check(lib.paged_decode_step_static(
+            out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), S, hq, hkv, d,
+            bs, mb, nb, int(max_context_len), float(scale), _dtype_code(q),
             _stream_handle(q.device)))
     return out
 

@@ -857,7 +857,35 @@ int waves_dim(int head_dim, int group) {
     }
 }
 
+// The scratch of the decode step that allocates nothing: a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code uses the
+// address hipGetSymbolAddress gives for the current device, never the
+// array's name (on the host that names a stand-in, not device memory).
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t *p, int64_t words) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
 }  // namespace
+
+void *static_scratch(int device, hipStream_t stream) {
+    constexpr int kMaxDev = 64;
+    static std::atomic<void *> ptrs[kMaxDev];
+    if (device < 0 || device >= kMaxDev) return nullptr;
+    void *p = ptrs[device].load(std::memory_order_acquire);
+    if (p) return p;
+    // first use on this device (the caller made it current): look the array
+    // up and clear its counter region; later calls leave the counters at zero
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
+    if (hipGetSymbolAddress((void **)&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    zero_fill_kernel<<<64, 256, 0, stream>>>(static_cast<uint32_t *>(p), (int64_t)(kStaticCounterBytes / 4));
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    ptrs[device].store(p, std::memory_order_release);
+    return p;
+}
 
 bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group) {
     const bool dt = dtype == 0 || dtype == 1 || dtype == 2;

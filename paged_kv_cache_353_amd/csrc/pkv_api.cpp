@@ -580,6 +580,41 @@ int paged_attn_decode(void *out, const void *q, const void *k_cache, const void 
                        workspace_bytes, stream);
 }
 
+int paged_decode_step_static(void *out, const void *q, const void *k_new, const void *v_new,
+                             void *k_cache, void *v_cache, const int32_t *block_tables,
+                             const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                             float scale, int32_t dtype, hipStream_t stream) {
+    if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_NULL;
+    bool one_query = false;
+    int st = decode_checks(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                           num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                           max_context_len, scale, dtype, &one_query);
+    if (st != PKV_OK) return st;
+    if (!one_query) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    const int32_t group = num_q_heads / num_kv_heads;
+    const int64_t waves = decode_grid_waves(dtype, head_dim, group);
+    if (waves <= 0) return PKV_ERR_HIP;
+    // the layout must fit the fixed array: counters in their fixed region,
+    // records of this call's sizes after it
+    const pkv::StaticScratchLayout lay = pkv::static_scratch_layout(num_seqs, num_kv_heads, group, head_dim, waves);
+    if (!lay.fits) return PKV_ERR_WORKSPACE;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return PKV_ERR_HIP;
+    char *w = static_cast<char *>(pkv::static_scratch(device, stream));
+    if (!w) return PKV_ERR_HIP;
+    const DecodeScratch s{reinterpret_cast<int32_t *>(w + lay.cnt_offset),
+                          reinterpret_cast<int32_t *>(w + lay.gcnt_offset),
+                          reinterpret_cast<float *>(w + lay.acc_offset), reinterpret_cast<float *>(w + lay.ml_offset),
+                          reinterpret_cast<float *>(w + lay.gacc_offset),
+                          reinterpret_cast<float *>(w + lay.gml_offset)};
+    return decode_launch(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len,
+                         scale, dtype, waves, s, stream);
+}
+
 int paged_decode_step(void *out, const void *q, const void *k_new, const void *v_new,
                       void *k_cache, void *v_cache, const int32_t *block_tables,
                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,

@@ -152,6 +152,40 @@ inline DecodeWorkspace decode_workspace(int32_t num_seqs, int32_t num_kv_heads, 
     return w;
 }
 
+// A fixed scratch area per GPU (a static device array) for the decode step
+// that allocates nothing.  Its counter region has a fixed place and size so
+// that the records of one call never land on the counters of another.
+constexpr int64_t kStaticMaxUnits = 16384;   // num_seqs * num_kv_heads
+constexpr int64_t kStaticMaxWaves = 1024;    // waves of the decode grid
+constexpr size_t kStaticScratchBytes = (size_t)24 << 20;
+constexpr size_t kStaticCounterBytes =
+    (((size_t)(kStaticMaxUnits + kStaticMaxWaves + kStaticMaxUnits) * sizeof(int32_t)) + 255) & ~(size_t)255;
+struct StaticScratchLayout {
+    size_t cnt_offset, gcnt_offset, acc_offset, ml_offset, gacc_offset, gml_offset, bytes;
+    bool fits;
+};
+inline StaticScratchLayout static_scratch_layout(int32_t num_seqs, int32_t num_kv_heads, int32_t group,
+                                                 int32_t head_dim, int64_t waves) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const int64_t units = (int64_t)num_seqs * num_kv_heads;
+    const size_t slots = (size_t)waves + (size_t)units;
+    const size_t acc_bytes = up(slots * (size_t)group * (size_t)head_dim * sizeof(float));
+    const size_t ml_bytes = up(slots * (size_t)group * 2 * sizeof(float));
+    StaticScratchLayout l{};
+    l.cnt_offset = 0;
+    l.gcnt_offset = (size_t)kStaticMaxUnits * sizeof(int32_t);
+    l.acc_offset = kStaticCounterBytes;
+    l.ml_offset = l.acc_offset + acc_bytes;
+    l.gacc_offset = l.ml_offset + ml_bytes;
+    l.gml_offset = l.gacc_offset + acc_bytes;
+    l.bytes = l.gml_offset + ml_bytes;
+    l.fits = units <= kStaticMaxUnits && waves <= kStaticMaxWaves && l.bytes <= kStaticScratchBytes;
+    return l;
+}
+// Device address of this GPU's scratch array (looked up once per device, its
+// counter region cleared on the given stream at that first use), or null.
+void *static_scratch(int device, hipStream_t stream);
+
 bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group);
 
 // Bytes of per-lane scratch (register spills) of the one-query kernel for this
