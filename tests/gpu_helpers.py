@@ -59,6 +59,14 @@ def gpu_step(inp: DecodeInputs, write=True, max_context_len=None, out=None):
     return out
 
 
+def unit_pairs(num_seqs: int, num_q_heads: int, num_kv_heads: int):
+    """One query head of every (sequence, KV head) unit, the head within the
+    group rotating with the sequence: each unit has its own split and merge,
+    so each is compared at least once."""
+    G = num_q_heads // num_kv_heads
+    return [(i, g * G + (i + g) % G) for i in range(num_seqs) for g in range(num_kv_heads)]
+
+
 def assert_close(got: torch.Tensor, want: np.ndarray, dtype: str, pairs=None, what=""):
     """Elementwise |d| <= atol + rtol |ref| and normwise ||d|| <= norm ||ref||
     per (sequence, head), over all outputs or the sampled pairs."""

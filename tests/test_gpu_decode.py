@@ -11,7 +11,7 @@ import torch
 
 import paged_kv_cache_353_amd as pkv
 from paged_kv_cache_353_amd import workloads as W
-from tests.gpu_helpers import assert_close, gpu_step, host_inputs, oracle_step, say
+from tests.gpu_helpers import assert_close, gpu_step, host_inputs, oracle_step, say, unit_pairs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -25,6 +25,7 @@ def _sample_pairs(inp, n, seed):
     # always include the longest and the shortest sequence
     pairs.add((int(np.argmax(inp.lens)), 0))
     pairs.add((int(np.argmin(inp.lens)), Hq - 1))
+    pairs.update(unit_pairs(S, Hq, inp.num_kv_heads))
     return sorted(pairs)
 
 
@@ -155,7 +156,7 @@ def test_long_context_sampled():
     h = host_inputs(inp)
     out = gpu_step(inp)
     assert torch.isfinite(out.float()).all()
-    pairs = [(0, 0), (1, 9), (2, 18), (3, 31), (3, 4), (2, 27)]
+    pairs = sorted({(0, 0), (1, 9), (2, 18), (3, 31), (3, 4), (2, 27)} | set(unit_pairs(4, 32, 8)))
     say("  running the oracle on sampled outputs")
     want = oracle_step(h, inp, pairs=pairs)
     worst = assert_close(out, want, "bf16", pairs=pairs, what="long context")
@@ -290,6 +291,30 @@ def test_workspace_reused_across_batches_and_left_zeroed():
             assert torch.count_nonzero(ws[:COUNTER_BYTES]).item() == 0, "arrival counters left non-zero"
             want = oracle_step(host_inputs(inp), inp, write=False)
             assert_close(out, want, "bf16", what=f"reuse rep {rep} S={inp.num_seqs}")
+
+
+def test_default_workspace_is_reused():
+    """Calls without a workspace share one per (device, stream): the second call
+    allocates nothing and gives the same bits."""
+    say("case: default workspace reuse")
+    inp = W.build_decode_inputs([3000, 17, 900, 1, 4096, 0, 2500], 32, 8, 128, 16, "bf16", 900,
+                                seed=24, device=DEV)
+    outs = []
+    for rep in range(3):
+        out = torch.empty_like(inp.q)
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated(DEV)
+        pkv.paged_attn_decode(out, inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                              inp.context_lens, inp.block_size, inp.scale,
+                              max_context_len=inp.max_context_len)
+        torch.cuda.synchronize()
+        if rep > 0:
+            assert torch.cuda.memory_allocated(DEV) == before, "a call without a workspace allocated"
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+    want = oracle_step(host_inputs(inp), inp, write=False)
+    assert_close(outs[0], want, "bf16", what="default workspace")
 
 
 def test_many_sequences_and_empty_ones():

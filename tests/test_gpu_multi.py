@@ -8,7 +8,7 @@ import torch
 import oracle
 import paged_kv_cache_353_amd as pkv
 from paged_kv_cache_353_amd import workloads as W
-from tests.gpu_helpers import assert_close, host_inputs, say
+from tests.gpu_helpers import assert_close, host_inputs, say, unit_pairs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -74,6 +74,8 @@ def test_multi_speculative_llama8b():
     rng = np.random.default_rng(75)
     triples = [(int(i), int(j), int(h)) for i, j, h in zip(rng.integers(0, 64, 300), rng.integers(0, 4, 300),
                                                            rng.integers(0, 32, 300))]
+    # and one output of every (sequence, KV head) unit, the query token rotating
+    triples = sorted(set(triples) | {(i, (i + h) % 4, h) for i, h in unit_pairs(64, 32, 8)})
     check_multi(inp, q4, triples=triples, what="speculative llama8b")
 
 
