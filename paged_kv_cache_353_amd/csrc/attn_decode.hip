@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // cache holds positions [0, L - 1) and the token itself comes from
     // k_new / v_new, into the registers of the unit's last sub-tile.
     const bool fused = a.k_new != nullptr;
-    const int fused_one = fused ? 1 : 0;
+    const int fused_one = uniform(fused ? 1 : 0);
 
     // contexts with no token: the output is the empty sum (sequence i is
     // written by wave i % W)
@@ -164,12 +164,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     const int64_t TA = (int64_t)T + (int64_t)C * NU * Hkv;   // augmented length
     const int Weff = C > 0 ? W : (T < W ? T : W);             // every wave below Weff gets >= 1 sub-tile
     if (wave >= Weff) return;
-    const int64_t x0 = TA * wave / Weff;                      // this wave's augmented range
-    const int64_t x1 = TA * (wave + 1) / Weff;
+    const double inv_weff = 1.0 / (double)Weff, inv_ta = 1.0 / (double)TA;
+    const int64_t x0 = floor_div(TA * wave, Weff, inv_weff);      // this wave's augmented range
+    const int64_t x1 = floor_div(TA * (wave + 1), Weff, inv_weff);
     // the wave whose range holds augmented position x: the largest w with
     // TA * w / Weff <= x
     auto wave_of = [&](int64_t x) -> int {
-        const int64_t w = ((x + 1) * Weff - 1) / TA;
+        const int64_t w = floor_div((x + 1) * Weff - 1, TA, inv_ta);
         return (int)(w < Weff - 1 ? w : Weff - 1);
     };
 
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // position inside the sequence: KV head, then sub-tile past the ghosts
     auto settle = [&](int64_t x, Cursor &u) -> int {
         const int64_t rem = x - ((int64_t)u.pre + (int64_t)C * u.cnt) * Hkv;
-        u.kvh = (int)(rem / (u.n + C));
+        u.kvh = (int)((uint32_t)rem / (uint32_t)(u.n + C));   // rem < Hkv * (n + C) < 2^32
         const int o = (int)(rem - (int64_t)u.kvh * (u.n + C)) - C;
         u.sub = o > 0 ? o : 0;
         return Hkv * u.pre + u.kvh * u.n + u.sub;
@@ -262,16 +263,22 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // the sub-tile at `u` ends the unit and holds the appended token of a fused step
     auto holds_new = [&](const Cursor &u) { return fused && u.sub + 1 == u.n; };
 
-    // Issues the K and V loads of the sub-tile at `u`; `live` false gives an
-    // empty range (loads return zeros and touch no memory), which keeps the
-    // number of loads in flight the same on every step.  The descriptors span
+    // Issues the K and V loads of the sub-tile at `u`.  The descriptors span
     // only the cached rows of the sub-tile, so rows past them read as zero.
-    auto issue = [&](const Cursor &u, bool live, u32x4 (&kr)[NL], u32x4 (&vr)[NL]) __attribute__((always_inline)) {
+    // The cached rows, L - fused_one - 16 sub, are never negative: a cursor
+    // moved past the range's end is given L = fused_one + 16 sub (`park`), an
+    // empty range whose loads return zeros and touch no memory, which keeps
+    // the number of loads in flight the same on every step.  (A clamp at zero
+    // here would be compiled to a vector med3.)
+    auto park = [&](Cursor &u) { u.L = fused_one + (u.sub << 4); };
+    auto issue = [&](const Cursor &u, u32x4 (&kr)[NL], u32x4 (&vr)[NL]) __attribute__((always_inline)) {
         const int t0 = u.sub << 4;
-        int rows = u.L - fused_one - t0;
+        // (The operands are taken through readfirstlane: kept in vector
+        // registers under register pressure, they would make this a vector
+        // computation whose temporary, a register of the buffer being
+        // refilled, costs a wait for every load in flight.)
+        int rows = uniform(u.L) - uniform(fused_one) - t0;
         rows = rows < 16 ? rows : 16;
-        rows = rows > 0 ? rows : 0;
-        rows = live ? rows : 0;
         const int64_t off = tile_offset(u);
         const int nbytes = uniform(rows * ROW);
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kc + off), 0, nbytes, kBufferFlags);
@@ -288,8 +295,14 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // hold the row (the others read zeros), and the result is OR-ed over the
     // zeros the cache descriptor returned for that row.
     u32x4 knew[NL], vnew[NL];
+    // The request is made kNewAhead issues before that of the unit's last
+    // sub-tile (the rows come from a small array that is not streamed and take
+    // longer to arrive), unless the previous unit's rows are still waiting to
+    // be used; then at the issue of the last sub-tile itself.
+    constexpr int kNewAhead = 2;
+    int new_unit = -1;   // the unit whose appended rows sit in (or are on their way to) knew/vnew
     auto issue_new = [&](const Cursor &u) __attribute__((always_inline)) {
-        const int rn = u.L - 1 - (u.sub << 4);   // row of the appended token
+        const int rn = u.L - 1 - ((u.n - 1) << 4);   // row of the appended token in the unit's last sub-tile
         const int64_t nb = uniform(((int64_t)u.seq * Hkv + u.kvh) * ROW);
         const __amdgpu_buffer_rsrc_t rkn = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(static_cast<const char *>(a.k_new) + nb), 0, ROW, kBufferFlags);
@@ -325,20 +338,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // Merges the four row-group streams of (m, l, acc); afterwards every lane
     // holds the totals: m, l for head (lane % 16), acc for its chunks.
     auto combine_rows = [&](float &m, float &l, float (&ac)[G][NCH][VEC], bool fold_half_rows) __attribute__((always_inline)) {
-        float M = fmaxf(m, xor16(m));
-        M = fmaxf(M, xor32(M, lane));
+        const float M = rows_max4(m);
         const float Mu = M == kNegInf ? 0.f : M;
         const float sc = fast_exp2(m - Mu);
-        float Ls = l * sc;
-        Ls += xor16(Ls);
-        Ls += xor32(Ls, lane);
+        const float Ls = rows_sum4(l * sc);
         static_for<0, G>([&]<int h>() {
             const float s = row_bcast<h>(sc);
             static_for<0, NCH>([&]<int ch>() {
                 static_for<0, VEC>([&]<int e>() {
-                    float x = ac[h][ch][e] * s;
-                    x += xor16(x);
-                    x += xor32(x, lane);
+                    float x = rows_sum4(ac[h][ch][e] * s);
                     if constexpr (R == 8) {
                         if (fold_half_rows) x += row_ror8(x);
                     }
@@ -632,6 +640,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             process_rows(u.L - (u.sub << 4), kr, vr);  // valid rows: >= 1
             return;
         }
+        new_unit = -1;   // knew / vnew are taken over below
         u32x4 k2[NL], v2[NL];
         static_for<0, NL>([&]<int b>() { k2[b] = kr[b] | knew[b]; v2[b] = vr[b] | vnew[b]; });
         process_rows(u.L - (u.sub << 4), k2, v2);
@@ -664,7 +673,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // that compute (whose count the compiler takes over both paths) does not
     // include them.
     auto issue_extras = [&](const Cursor &u, int gidx) __attribute__((always_inline)) {
-        if (holds_new(u)) issue_new(u);
+        if (fused && u.sub + 1 + kNewAhead >= u.n && new_unit < 0) {
+            issue_new(u);
+            new_unit = unit_of(u);
+        }
         prefetch_q(u, gidx);
     };
 
@@ -685,15 +697,17 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     Cursor cl = cur;   // the most recently issued sub-tile ...
     int gl = g0;       // ... and its index
     load_q(cur, qr);
-    issue(cl, true, kbuf[0], vbuf[0]);
+    issue(cl, kbuf[0], vbuf[0]);
     issue_extras(cl, gl);
     static_for<1, kDepth - 1>([&]<int m>() {
         const bool more = gl + 1 < g1;
         if (more) {
             advance(cl);
             ++gl;
+        } else {
+            park(cl);
         }
-        issue(cl, more, kbuf[m], vbuf[m]);
+        issue(cl, kbuf[m], vbuf[m]);
         if (more) issue_extras(cl, gl);
     });
     reset_state();
@@ -703,64 +717,70 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     int arrive_at = -1;     // ... whose arrival is posted once sub-tile arrive_at is consumed
     int pend_old = 0;       // the count it returned (lane 0)
     Split psplit{};
-    bool stop = false;
-    while (!stop) {
-        static_for<0, kDepth>([&]<int i>() {
-            if (stop) return;
-            constexpr int nb = (i + kDepth - 1) % kDepth;
-            const bool more = gl + 1 < g1;
-            if (more) {
-                advance(cl);
-                ++gl;
-            }
-            issue(cl, more, kbuf[nb], vbuf[nb]);
-            process(cp, kbuf[i], vbuf[i]);
-            if (g == arrive_at) {
-                // The loads of this sub-tile were issued after the record's
-                // stores and have been consumed, and vector memory accesses
-                // complete in issue order: the stores are complete.  The
-                // arrival's count is read at the end of the range.
-                asm volatile("" ::"v"(acc[0][0][0]), "v"(l_run) : "memory");
-                __builtin_amdgcn_sched_barrier(0);
-                pend_old = post_arrival(psplit);
-                arrive_at = -1;
-            }
-            if (g + 1 == g1) {
-                stop = true;
-                return;
-            }
-            if (cp.sub + 1 == cp.n) {
-                // a segment ends inside the range
-                combine_rows(m_run, l_run, acc, true);
-                const int ua = Hkv * cp.pre + cp.kvh * cp.n;
-                if (seg_first == ua) {
-                    write_out(cp, acc, l_run);
-                } else {
-                    psplit = split_of(cp);
-                    store_record(psplit);
-                    // keep the record's stores ahead of the next sub-tile's loads
-                    asm volatile("" ::: "memory");
-                    __builtin_amdgcn_sched_barrier(0);
-                    pend = true;
-                    arrive_at = gl + 1;
-                }
-                advance(cp);
-                ++g;
-                seg_first = g;
-                if (qn_unit == unit_of(cp)) {
-                    static_for<0, NL>([&]<int b>() { qr[b] = qn[b]; });
-                    qn_unit = -1;
-                } else {
-                    load_q(cp, qr);
-                }
-                reset_state();
+    // One step; returns true once sub-tile g1 - 1 has been consumed.  (The loop
+    // leaves from the step that ends it, so that its back edge follows a full
+    // round of steps, where every buffer's loads have been consumed: the
+    // compiler's wait analysis then sees no load in flight into a buffer being
+    // refilled.)
+    auto step = [&]<int i>() __attribute__((always_inline)) -> bool {
+        constexpr int nb = (i + kDepth - 1) % kDepth;
+        const bool more = gl + 1 < g1;
+        if (more) {
+            advance(cl);
+            ++gl;
+        } else {
+            park(cl);   // past the range's end: an empty load range
+        }
+        issue(cl, kbuf[nb], vbuf[nb]);
+        process(cp, kbuf[i], vbuf[i]);
+        if (g == arrive_at) {
+            // The loads of this sub-tile were issued after the record's
+            // stores and have been consumed, and vector memory accesses
+            // complete in issue order: the stores are complete.  The
+            // arrival's count is read at the end of the range.
+            asm volatile("" ::"v"(acc[0][0][0]), "v"(l_run) : "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            pend_old = post_arrival(psplit);
+            arrive_at = -1;
+        }
+        if (g + 1 == g1) return true;
+        if (cp.sub + 1 == cp.n) {
+            // a segment ends inside the range
+            combine_rows(m_run, l_run, acc, true);
+            const int ua = Hkv * cp.pre + cp.kvh * cp.n;
+            if (seg_first == ua) {
+                write_out(cp, acc, l_run);
             } else {
-                advance(cp);
-                ++g;
+                psplit = split_of(cp);
+                store_record(psplit);
+                // keep the record's stores ahead of the next sub-tile's loads
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                pend = true;
+                arrive_at = gl + 1;
             }
-            if (more) issue_extras(cl, gl);
-        });
-    }
+            advance(cp);
+            ++g;
+            seg_first = g;
+            if (qn_unit == unit_of(cp)) {
+                static_for<0, NL>([&]<int b>() { qr[b] = qn[b]; });
+                qn_unit = -1;
+            } else {
+                // not requested ahead (a unit of one sub-tile before it):
+                // wait here, so that no path reaches the next step with q
+                // loads in flight and every step's waits stay exact
+                load_q(cp, qr);
+                wait_vmem_done();
+            }
+            reset_state();
+        } else {
+            advance(cp);
+            ++g;
+        }
+        if (more) issue_extras(cl, gl);
+        return false;
+    };
+    while (!static_any<0, kDepth>(step)) {}
 
     // ---- the range's last segment (sub-tile g1 - 1 was the last consumed)
     combine_rows(m_run, l_run, acc, true);

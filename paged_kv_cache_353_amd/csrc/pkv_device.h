@@ -33,6 +33,18 @@ __device__ __forceinline__ void static_for(F &&f) {
         static_for<I + 1, N>(f);
     }
 }
+// f<I>(), f<I + 1>(), ... f<N - 1>() until one returns true; returns whether
+// one did.  A loop `while (!static_any<0, N>(step))` leaves straight from the
+// step that ends it, so its back edge is reached only after all N steps.
+template <int I, int N, typename F>
+__device__ __forceinline__ bool static_any(F &&f) {
+    if constexpr (I < N) {
+        if (f.template operator()<I>()) return true;
+        return static_any<I + 1, N>(f);
+    } else {
+        return false;
+    }
+}
 
 // Element reinterpretation goes through by-value helpers: hipcc (clang 22)
 // miscompiles __builtin_bit_cast applied directly to an ext-vector element
@@ -73,6 +85,44 @@ __device__ __forceinline__ float row_bcast_split(float lo, float hi) {
 __device__ __forceinline__ float row_ror8(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
         0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+// floor(num / den) for 0 <= num < 2^52 and 0 < den < 2^52, given inv_den =
+// 1.0 / den: the fp64 product is within one of the quotient, and one exact
+// integer correction each way makes it exact (no 64-bit integer division).
+__device__ __forceinline__ int64_t floor_div(int64_t num, int64_t den, double inv_den) {
+    int64_t q = (int64_t)((double)num * inv_den);
+    if (q * den > num) --q;
+    else if ((q + 1) * den <= num) ++q;
+    return q;
+}
+
+// Lane swaps between 16-lane rows (gfx950 VALU instructions, no LDS).
+// swap_rows16(a, b): rows 1 and 3 of a trade places with rows 0 and 2 of b,
+// so that with a == b == x afterwards a holds x of rows 0, 0, 2, 2 and b x of
+// rows 1, 1, 3, 3.  swap_rows32(a, b): the upper half of a trades with the
+// lower half of b (a: x of the lower half everywhere, b: of the upper).
+// The leading s_nop covers the wait a VALU write needs before these read it.
+__device__ __forceinline__ void swap_rows16(float &a, float &b) {
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_rows32(float &a, float &b) {
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+// x summed over lanes l, l ^ 16, l ^ 32 and l ^ 48, as (r0 + r1) + (r2 + r3)
+// of the four rows, in every lane.
+__device__ __forceinline__ float rows_sum4(float x) {
+    float a = x, b = x;
+    swap_rows16(a, b);
+    float c = a + b, d = c;
+    swap_rows32(c, d);
+    return c + d;
+}
+__device__ __forceinline__ float rows_max4(float x) {
+    float a = x, b = x;
+    swap_rows16(a, b);
+    float c = fmaxf(a, b), d = c;
+    swap_rows32(c, d);
+    return fmaxf(c, d);
 }
 __device__ __forceinline__ float xor16(float x) {  // lane ^ 16
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
