@@ -30,7 +30,9 @@
 // shared out in equal contiguous ranges, one per resident wave.  Units split
 // between waves, and in the shared-prefix case every unit, leave partial
 // records; a second, short launch merges them in a fixed order with every
-// record of an output in flight at once.  Loads use descriptors that span
+// record of an output in flight at once.  K and V are streamed with the
+// non-temporal policy (read once, kept out of the way of the records and
+// tables in the caches).  Loads use descriptors that span
 // only the unit's valid rows, so rows past the end read as zero, and every
 // score outside a column's window is set to -inf before the exponential, so
 // stale cache contents never reach the result.
@@ -455,15 +457,15 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
         const int nbytes = uniform(rows * ROW);
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kc + off), 0, nbytes, kBufferFlags);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vc + off), 0, nbytes, kBufferFlags);
-        static_for<0, NLK>([&]<int b>() { kr[b] = load_chunk(rk, koff + 64 * b); });
+        static_for<0, NLK>([&]<int b>() { kr[b] = load_stream(rk, koff + 64 * b); });
         static_for<0, 4>([&]<int m>() {
             if constexpr (VW == 2) {
-                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + m * ROW, 0, 0));
+                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff + m * ROW, 0, kStreamNT));
                 vr[m].w[0] = x[0];
                 vr[m].w[1] = x[1];
             } else {
                 static_for<0, VW / 4>([&]<int h>() {
-                    const u32x4 x = load_chunk(rv, voff + m * ROW + 16 * h);
+                    const u32x4 x = load_stream(rv, voff + m * ROW + 16 * h);
                     static_for<0, 4>([&]<int k>() { vr[m].w[4 * h + k] = x[k]; });
                 });
             }
