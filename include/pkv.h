@@ -220,7 +220,8 @@ int paged_decode_step(void *out, const void *q, const void *k_new, const void *v
  *   (about (1024 + units) * group * head_dim * 8 bytes)  -> PKV_ERR_WORKSPACE
  *   configurations that paged_decode_step serves with its many-column kernel
  *   (group sizes other than 1, 2, 4, 8, and those whose one-query kernel
- *   would spill registers: at present bf16 with group 8)
+ *   would spill registers: at present bf16 with group 8, and fp32 at
+ *   head_dim 128 with group 8)
  *                                                       -> PKV_ERR_UNSUPPORTED
  *   first call on a device under stream capture         -> PKV_ERR_HIP
  */

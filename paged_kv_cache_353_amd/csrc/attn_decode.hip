@@ -23,9 +23,10 @@
 // un-normalised output) in the workspace, and the wave that arrives last at
 // the unit's counter merges them in a fixed order and writes the output.  The
 // counter is reset to zero by that wave, so the workspace is left as it was
-// found.  A wave reports the arrival of its first segment one sub-tile after
-// writing its record, without waiting for the count, and acts on the count at
-// the end of its range: the boundary costs the stream no round trip.
+// found.  A wave whose range begins inside a unit keeps that first segment's
+// state in registers and writes it as a record only at the end of its range,
+// with the last segment's: records are written through to memory, and a
+// store in the middle of the stream would hold up every load issued after it.
 //
 // One wave, one sub-tile (16 tokens of one KV head, the G query heads that
 // share it):
@@ -64,7 +65,7 @@ constexpr int kDirectMerge = 8;  // units split in at most this many pieces merg
 // output), in sub-tiles of streaming.  The split charges it to the wave whose
 // range holds the start of a unit.
 #ifndef PKV_UNIT_COST
-#define PKV_UNIT_COST 3
+#define PKV_UNIT_COST 4
 #endif
 constexpr int kUnitCost = PKV_UNIT_COST;
 #ifndef PKV_DEPTH
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // sub-tile (the rows come from a small array that is not streamed and take
     // longer to arrive), unless the previous unit's rows are still waiting to
     // be used; then at the issue of the last sub-tile itself.
-    constexpr int kNewAhead = 2;
+    constexpr int kNewAhead = NL <= 4 ? 2 : 0;   // (fp32 rows take twice the registers)
     int new_unit = -1;   // the unit whose appended rows sit in (or are on their way to) knew/vnew
     auto issue_new = [&](const Cursor &u) __attribute__((always_inline)) {
         const int rn = u.L - 1 - ((u.n - 1) << 4);   // row of the appended token in the unit's last sub-tile
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         return tr;
     };
     // this segment's record
-    auto store_record = [&](const Split &s) __attribute__((always_inline)) {
+    auto store_record = [&](const Split &s, const float (&sa)[G][NCH][VEC], float sm, float sl) __attribute__((always_inline)) {
         const int64_t slot = (int64_t)wave + s.unit;
         float *pacc = a.ws_acc + slot * G * D;
         float *pml = a.ws_ml + slot * G * 2;
@@ -544,16 +545,16 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             static_for<0, NCH>([&]<int ch>() {
                 if (chunk_writer) {
                     static_for<0, VEC / 4>([&]<int v4>() {
-                        const f32x4 x = {acc[h][ch][4 * v4], acc[h][ch][4 * v4 + 1], acc[h][ch][4 * v4 + 2],
-                                         acc[h][ch][4 * v4 + 3]};
+                        const f32x4 x = {sa[h][ch][4 * v4], sa[h][ch][4 * v4 + 1], sa[h][ch][4 * v4 + 2],
+                                         sa[h][ch][4 * v4 + 3]};
                         store_coherent(pacc, kRecAcc, (h * D + chunk_of(ch) * VEC + 4 * v4) * 4, x);
                     });
                 }
             });
         });
         if (rg == 0 && c < G) {
-            store_coherent_f32(pml, G * 8, 8 * c, m_run);
-            store_coherent_f32(pml, G * 8, 8 * c + 4, l_run);
+            store_coherent_f32(pml, G * 8, 8 * c, sm);
+            store_coherent_f32(pml, G * 8, 8 * c + 4, sl);
         }
     };
     // The arrival of a segment: a relaxed agent-scope add on the unit's (or
@@ -687,11 +688,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // that the buffers rotate without moves.  A segment (the part of a unit
     // inside the range) that ends before the range does is finished in the
     // loop: a whole unit writes its output; the range's first segment, when
-    // its unit began in an earlier range, writes a partial record and reports
-    // its arrival a few sub-tiles later, once the record's stores are known to
-    // be complete (vector memory accesses complete in issue order, and loads
-    // issued after the stores have then returned).  The range's last segment
-    // is finished after the loop, where any merge this wave owes happens.
+    // its unit began in an earlier range, is set aside (its combined state
+    // held in registers).  After the loop the range's last segment and the
+    // set-aside one are written as records, their arrivals posted, and any
+    // merge this wave owes done.
     u32x4 kbuf[kDepth][NL], vbuf[kDepth][NL];
     Cursor cp = cur;   // the sub-tile being consumed (g)
     Cursor cl = cur;   // the most recently issued sub-tile ...
@@ -713,10 +713,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     reset_state();
     int g = g0;
     int seg_first = g0;
-    bool pend = false;      // the range's first segment left a record ...
-    int arrive_at = -1;     // ... whose arrival is posted once sub-tile arrive_at is consumed
-    int pend_old = 0;       // the count it returned (lane 0)
+    bool pend = false;      // the range's first segment ends inside the range (unit begun earlier)
     Split psplit{};
+    // its state, stored as a record at the end of the range when it fits in
+    // registers beside the running state (up to 32 accumulators)
+    constexpr bool kHoldFirst = G * NCH * VEC <= 32;
+    float hacc[G][NCH][VEC];
+    float hm = 0.f, hl = 0.f;
     // One step; returns true once sub-tile g1 - 1 has been consumed.  (The loop
     // leaves from the step that ends it, so that its back edge follows a full
     // round of steps, where every buffer's loads have been consumed: the
@@ -733,16 +736,6 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         }
         issue(cl, kbuf[nb], vbuf[nb]);
         process(cp, kbuf[i], vbuf[i]);
-        if (g == arrive_at) {
-            // The loads of this sub-tile were issued after the record's
-            // stores and have been consumed, and vector memory accesses
-            // complete in issue order: the stores are complete.  The
-            // arrival's count is read at the end of the range.
-            asm volatile("" ::"v"(acc[0][0][0]), "v"(l_run) : "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            pend_old = post_arrival(psplit);
-            arrive_at = -1;
-        }
         if (g + 1 == g1) return true;
         if (cp.sub + 1 == cp.n) {
             // a segment ends inside the range
@@ -751,13 +744,22 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             if (seg_first == ua) {
                 write_out(cp, acc, l_run);
             } else {
+                // the range's first segment, of a unit begun in an earlier
+                // range: its state is held to the end of the range (stored
+                // now where holding it would not fit in registers)
                 psplit = split_of(cp);
-                store_record(psplit);
-                // keep the record's stores ahead of the next sub-tile's loads
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (kHoldFirst) {
+                    static_for<0, G>([&]<int h>() {
+                        static_for<0, NCH>([&]<int ch>() {
+                            static_for<0, VEC>([&]<int e>() { hacc[h][ch][e] = acc[h][ch][e]; });
+                        });
+                    });
+                    hm = m_run;
+                    hl = l_run;
+                } else {
+                    store_record(psplit, acc, m_run, l_run);
+                }
                 pend = true;
-                arrive_at = gl + 1;
             }
             advance(cp);
             ++g;
@@ -791,13 +793,14 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         write_out(cp, acc, l_run);
     } else {
         lsplit = split_of(cp);
-        store_record(lsplit);
+        store_record(lsplit, acc, m_run, l_run);
     }
+    if (kHoldFirst && pend) store_record(psplit, hacc, hm, hl);
     if (last_whole && !pend) return;
     wait_vmem_done();   // the records' stores are complete
-    int last_old = 0;
+    int last_old = 0, pend_old = 0;
     if (!last_whole) last_old = post_arrival(lsplit);
-    if (pend && arrive_at >= 0) pend_old = post_arrival(psplit);
+    if (pend) pend_old = post_arrival(psplit);
     if (!last_whole) complete(lsplit, __builtin_amdgcn_readlane(last_old, 0));
     if (pend) complete(psplit, __builtin_amdgcn_readlane(pend_old, 0));
 }
