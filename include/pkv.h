@@ -219,9 +219,8 @@ int paged_decode_step(void *out, const void *q, const void *k_new, const void *v
  *   units plus one per wave of the grid fit the array
  *   (about (1024 + units) * group * head_dim * 8 bytes)  -> PKV_ERR_WORKSPACE
  *   configurations that paged_decode_step serves with its many-column kernel
- *   (group sizes other than 1, 2, 4, 8, and those whose one-query kernel
- *   would spill registers: at present bf16 with group 8, and fp32 at
- *   head_dim 128 with group 8)
+ *   (group sizes other than 1, 2, 4, 8, and any whose one-query kernel
+ *   would spill registers: none at present)
  *                                                       -> PKV_ERR_UNSUPPORTED
  *   first call on a device under stream capture         -> PKV_ERR_HIP
  */

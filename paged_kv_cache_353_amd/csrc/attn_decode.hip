@@ -336,43 +336,67 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         });
     };
 
-    // Merges the four row-group streams of (m, l, acc); afterwards every lane
-    // holds the totals: m, l for head (lane % 16), acc for its chunks.
-    auto combine_rows = [&](float &m, float &l, float (&ac)[G][NCH][VEC], bool fold_half_rows) __attribute__((always_inline)) {
+    // Merges the four row-group streams of (m, l, acc).  m and l end up in
+    // every lane (head = lane % 16); the acc totals are scattered over the
+    // rows: of the lane's G * NCH * VEC accumulators, taken in (head, chunk
+    // slot, element) order, row r keeps the totals of the r-th quarter (Q
+    // values, in runs of RL consecutive elements of one head's chunk), so
+    // that the rows share the stores of the results.
+    constexpr int NV = G * NCH * VEC;
+    constexpr int Q = NV / 4;
+    constexpr int RL = Q < VEC ? Q : VEC;
+    constexpr int NRUN = Q / RL;
+    static_assert(NV % 4 == 0 && Q % RL == 0, "accumulators split in four quarters of whole runs");
+    auto combine_rows = [&](float &m, float &l, const float (&ac)[G][NCH][VEC], float (&tot)[Q]) __attribute__((always_inline)) {
         const float M = rows_max4(m);
         const float Mu = M == kNegInf ? 0.f : M;
         const float sc = fast_exp2(m - Mu);
         const float Ls = rows_sum4(l * sc);
+        float v[NV];
         static_for<0, G>([&]<int h>() {
             const float s = row_bcast<h>(sc);
             static_for<0, NCH>([&]<int ch>() {
-                static_for<0, VEC>([&]<int e>() {
-                    float x = rows_sum4(ac[h][ch][e] * s);
-                    if constexpr (R == 8) {
-                        if (fold_half_rows) x += row_ror8(x);
-                    }
-                    ac[h][ch][e] = x;
-                });
+                static_for<0, VEC>([&]<int e>() { v[(h * NCH + ch) * VEC + e] = ac[h][ch][e] * s; });
             });
+        });
+        static_for<0, Q>([&]<int q>() {
+            float x = rows_scatter_sum4(v[q], v[q + Q], v[q + 2 * Q], v[q + 3 * Q]);
+            // 8 chunks a row: lanes c and c + 8 hold the two token halves of one chunk
+            if constexpr (R == 8) x += row_ror8(x);
+            tot[q] = x;
         });
         m = M;
         l = Ls;
     };
 
-    // Chunk index (within a row) of accumulator chunk `ch` of this lane.
+    // Chunk index (within a row) of accumulator chunk slot `ch` of this lane.
     auto chunk_of = [&](int ch) { return R == 32 ? ch * 16 + c : (R == 8 ? (c & 7) : c); };
-    const bool chunk_writer = R == 8 ? (rg == 0 && c < 8) : rg == 0;
+    // lanes that write their totals (with 8 chunks a row, lanes c and c + 8 hold the same)
+    const bool writer = R == 8 ? c < 8 : true;
+    // run j of this lane's quarter: head, chunk slot and first element
+    struct Run { int h, ch, e0; };
+    auto run_of = [&](int j) -> Run {
+        const int idx0 = rg * Q + j * RL;
+        return Run{idx0 / (NCH * VEC), (idx0 / VEC) % NCH, idx0 % VEC};
+    };
 
-    auto write_out = [&](const Cursor &u, const float (&ac)[G][NCH][VEC], float l) {
+    auto write_out = [&](const Cursor &u, const float (&tot)[Q], float l) {
         char *ob = static_cast<char *>(a.out) + ((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW;
-        static_for<0, G>([&]<int h>() {
-            const float inv = 1.f / row_bcast<h>(l);
-            static_for<0, NCH>([&]<int ch>() {
-                float f[VEC];
-                static_for<0, VEC>([&]<int e>() { f[e] = ac[h][ch][e] * inv; });
-                const u32x4 pk = pack_chunk<DT>(f);
-                if (chunk_writer) store_chunk(ob, G * ROW, h * ROW + chunk_of(ch) * 16, pk);
-            });
+        static_for<0, NRUN>([&]<int j>() {
+            const Run r = run_of(j);
+            // the exp-sum of head r.h sits in lane r.h of every row
+            const float L = __builtin_bit_cast(
+                float, __builtin_amdgcn_ds_bpermute(((lane & ~15) + r.h) << 2, __builtin_bit_cast(int, l)));
+            const float inv = 1.f / L;
+            float f[16 / EB] = {};
+            static_for<0, RL>([&]<int t>() { f[t] = tot[j * RL + t] * inv; });
+            const u32x4 pk = pack_chunk<DT>(f);
+            const int off = r.h * ROW + chunk_of(r.ch) * 16 + r.e0 * EB;
+            if (writer) {
+                if constexpr (RL * EB == 16) store_chunk(ob, G * ROW, off, pk);
+                else if constexpr (RL * EB == 8) store_b64(ob, G * ROW, off, pk[0], pk[1]);
+                else store_b32(ob, G * ROW, off, pk[0]);
+            }
         });
     };
 
@@ -537,20 +561,24 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         return tr;
     };
     // this segment's record
-    auto store_record = [&](const Split &s, const float (&sa)[G][NCH][VEC], float sm, float sl) __attribute__((always_inline)) {
+    auto store_record = [&](const Split &s, const float (&sa)[Q], float sm, float sl) __attribute__((always_inline)) {
         const int64_t slot = (int64_t)wave + s.unit;
         float *pacc = a.ws_acc + slot * G * D;
         float *pml = a.ws_ml + slot * G * 2;
-        static_for<0, G>([&]<int h>() {
-            static_for<0, NCH>([&]<int ch>() {
-                if (chunk_writer) {
-                    static_for<0, VEC / 4>([&]<int v4>() {
-                        const f32x4 x = {sa[h][ch][4 * v4], sa[h][ch][4 * v4 + 1], sa[h][ch][4 * v4 + 2],
-                                         sa[h][ch][4 * v4 + 3]};
-                        store_coherent(pacc, kRecAcc, (h * D + chunk_of(ch) * VEC + 4 * v4) * 4, x);
+        static_for<0, NRUN>([&]<int j>() {
+            const Run r = run_of(j);
+            const int off = (r.h * D + chunk_of(r.ch) * VEC + r.e0) * 4;
+            if (writer) {
+                if constexpr (RL >= 4) {
+                    static_for<0, RL / 4>([&]<int k>() {
+                        const f32x4 x = {sa[j * RL + 4 * k], sa[j * RL + 4 * k + 1], sa[j * RL + 4 * k + 2],
+                                         sa[j * RL + 4 * k + 3]};
+                        store_coherent(pacc, kRecAcc, off + 16 * k, x);
                     });
+                } else {
+                    static_for<0, RL>([&]<int k>() { store_coherent_f32(pacc, kRecAcc, off + 4 * k, sa[j * RL + k]); });
                 }
-            });
+            }
         });
         if (rg == 0 && c < G) {
             store_coherent_f32(pml, G * 8, 8 * c, sm);
@@ -715,10 +743,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     int seg_first = g0;
     bool pend = false;      // the range's first segment ends inside the range (unit begun earlier)
     Split psplit{};
-    // its state, stored as a record at the end of the range when it fits in
-    // registers beside the running state (up to 32 accumulators)
-    constexpr bool kHoldFirst = G * NCH * VEC <= 32;
-    float hacc[G][NCH][VEC];
+    float hacc[Q];             // its state (this lane's quarter), stored as a record at the end of the range
     float hm = 0.f, hl = 0.f;
     // One step; returns true once sub-tile g1 - 1 has been consumed.  (The loop
     // leaves from the step that ends it, so that its back edge follows a full
@@ -739,26 +764,18 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         if (g + 1 == g1) return true;
         if (cp.sub + 1 == cp.n) {
             // a segment ends inside the range
-            combine_rows(m_run, l_run, acc, true);
+            float tot[Q];
+            combine_rows(m_run, l_run, acc, tot);
             const int ua = Hkv * cp.pre + cp.kvh * cp.n;
             if (seg_first == ua) {
-                write_out(cp, acc, l_run);
+                write_out(cp, tot, l_run);
             } else {
                 // the range's first segment, of a unit begun in an earlier
-                // range: its state is held to the end of the range (stored
-                // now where holding it would not fit in registers)
+                // range: its state is held to the end of the range
                 psplit = split_of(cp);
-                if constexpr (kHoldFirst) {
-                    static_for<0, G>([&]<int h>() {
-                        static_for<0, NCH>([&]<int ch>() {
-                            static_for<0, VEC>([&]<int e>() { hacc[h][ch][e] = acc[h][ch][e]; });
-                        });
-                    });
-                    hm = m_run;
-                    hl = l_run;
-                } else {
-                    store_record(psplit, acc, m_run, l_run);
-                }
+                static_for<0, Q>([&]<int q>() { hacc[q] = tot[q]; });
+                hm = m_run;
+                hl = l_run;
                 pend = true;
             }
             advance(cp);
@@ -785,17 +802,18 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     while (!static_any<0, kDepth>(step)) {}
 
     // ---- the range's last segment (sub-tile g1 - 1 was the last consumed)
-    combine_rows(m_run, l_run, acc, true);
+    float tot[Q];
+    combine_rows(m_run, l_run, acc, tot);
     const int ua_last = Hkv * cp.pre + cp.kvh * cp.n;
     const bool last_whole = seg_first == ua_last && g + 1 == ua_last + cp.n;
     Split lsplit{};
     if (last_whole) {
-        write_out(cp, acc, l_run);
+        write_out(cp, tot, l_run);
     } else {
         lsplit = split_of(cp);
-        store_record(lsplit, acc, m_run, l_run);
+        store_record(lsplit, tot, m_run, l_run);
     }
-    if (kHoldFirst && pend) store_record(psplit, hacc, hm, hl);
+    if (pend) store_record(psplit, hacc, hm, hl);
     if (last_whole && !pend) return;
     wait_vmem_done();   // the records' stores are complete
     int last_old = 0, pend_old = 0;

@@ -215,9 +215,8 @@ int decode_checks(const void *out, const void *q, const void *k_new, const void 
     const int32_t group = num_q_heads / num_kv_heads;
     // The one-query kernel serves group sizes 1, 2, 4 and 8 where it keeps
     // its state in registers; other group sizes, and configurations whose
-    // compiled kernel spills (at present bf16 with 8 query heads per KV head,
-    // and fp32 at head_dim 128 with 8; a spilling build ran about ten times
-    // slower), go to the many-column kernel.
+    // compiled kernel would spill (none at present; a spilling build ran
+    // about ten times slower), go to the many-column kernel.
     *one_query = pkv::decode_supported(dtype, head_dim, group) && block_size % 16 == 0 && block_size <= 256 &&
                  !(num_seqs > 0 && pkv::decode_scratch_bytes(dtype, head_dim, group) > 0);
     if (!*one_query) return PKV_OK;

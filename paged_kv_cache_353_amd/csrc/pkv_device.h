@@ -117,6 +117,16 @@ __device__ __forceinline__ float rows_sum4(float x) {
     swap_rows32(c, d);
     return c + d;
 }
+// Four values reduced over the four rows at once: afterwards row r holds the
+// sum, over the rows, of the r-th argument, as (r0 + r1) + (r2 + r3).
+__device__ __forceinline__ float rows_scatter_sum4(float x, float y, float z, float w) {
+    swap_rows16(x, y);   // x: x0, y0, x2, y2 by rows; y: x1, y1, x3, y3
+    float s1 = x + y;    // rows 0..3: x0+x1, y0+y1, x2+x3, y2+y3
+    swap_rows16(z, w);
+    float s2 = z + w;    // rows 0..3: z0+z1, w0+w1, z2+z3, w2+w3
+    swap_rows32(s1, s2);
+    return s1 + s2;      // rows 0..3: x, y, z, w summed over the rows
+}
 __device__ __forceinline__ float rows_max4(float x) {
     float a = x, b = x;
     swap_rows16(a, b);
@@ -243,6 +253,16 @@ __device__ __forceinline__ void store_coherent_f32(float *base, int bytes, int b
 __device__ __forceinline__ void store_chunk(void *base, int bytes, int byte_off, const u32x4 &v) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufferFlags);
     __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
+}
+// Plain 8- and 4-byte stores through a buffer descriptor.
+__device__ __forceinline__ void store_b64(void *base, int bytes, int byte_off, uint32_t lo, uint32_t hi) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufferFlags);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void store_b32(void *base, int bytes, int byte_off, uint32_t v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kBufferFlags);
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, byte_off, 0, 0);
 }
 // Relaxed agent-scope atomic add that returns the previous value, issued as
 // a buffer instruction: the compiler then counts it in order with the

@@ -124,9 +124,9 @@ def test_fused_step_long_context_sampled():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("Hq,Hkv", [(24, 8), (12, 2), (32, 2), (16, 1), (64, 8)])
 def test_other_group_sizes_step_and_decode(dtype, Hq, Hkv):
-    """Group sizes the one-query kernel does not hold in registers (3, 6, 16,
-    and 8 at head_dim 128) go through the many-column kernel, with the append
-    written first in a fused step."""
+    """Group sizes the one-query kernel does not serve (3, 6, 16) go through
+    the many-column kernel, with the append written first in a fused step;
+    group 8 at head_dim 128 runs on the one-query kernel."""
     say(f"case: group size {Hq // Hkv} dtype={dtype} (step, then decode)")
     lens = [1, 2, 17, 300, 1500]
     inp = W.build_decode_inputs(lens, Hq, Hkv, 128, 16, dtype, 200, seed=120 + Hq, device=DEV)
