@@ -741,6 +741,10 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     reset_state();
     int g = g0;
     int seg_first = g0;
+    // the split of the current unit, when a record of it may be needed (the
+    // range's first unit, and a later one that runs past the range's end):
+    // worked out while loads are in flight rather than when the record is due
+    Split usplit = split_of(cur);
     bool pend = false;      // the range's first segment ends inside the range (unit begun earlier)
     Split psplit{};
     float hacc[Q];             // its state (this lane's quarter), stored as a record at the end of the range
@@ -772,7 +776,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             } else {
                 // the range's first segment, of a unit begun in an earlier
                 // range: its state is held to the end of the range
-                psplit = split_of(cp);
+                psplit = usplit;
                 static_for<0, Q>([&]<int q>() { hacc[q] = tot[q]; });
                 hm = m_run;
                 hl = l_run;
@@ -781,6 +785,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
             advance(cp);
             ++g;
             seg_first = g;
+            if (g + cp.n > g1) usplit = split_of(cp);   // the range's last segment, partial
             if (qn_unit == unit_of(cp)) {
                 static_for<0, NL>([&]<int b>() { qr[b] = qn[b]; });
                 qn_unit = -1;
@@ -810,7 +815,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     if (last_whole) {
         write_out(cp, tot, l_run);
     } else {
-        lsplit = split_of(cp);
+        lsplit = usplit;
         store_record(lsplit, tot, m_run, l_run);
     }
     if (pend) store_record(psplit, hacc, hm, hl);
