@@ -646,6 +646,13 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             if (orow[ch] >= 0) store_record(ra, rm, 0, ch * kMultiCols + c, m[ch], l[ch], ac[ch], false);
         });
     };
+    // The range's first segment, when its unit began in an earlier range and
+    // ends inside this one, is held until the end of the range (one column
+    // chunk only: two would not fit the registers).
+    constexpr bool kHoldFirst = CH == 1;
+    float hm[CH], hl[CH];
+    f32x4 hacc[CH][DL];
+    int64_t hslot = -1;
     // Leaves the unit at `u` after sub-tile `g_last`.
     //  * multi mode: a unit inside this wave's range is finished here; a unit
     //    split between k waves leaves k records (one per wave, at slot
@@ -693,6 +700,21 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             });
             return;
         }
+        if constexpr (kHoldFirst) {
+            if (seg_first != ua && g_last + 1 < g1) {
+                // the range's first segment, of a unit begun in an earlier
+                // range, ending inside the range: held in registers and
+                // written at the end of the range (a store burst in the
+                // middle of the stream holds up the loads queued behind it)
+                static_for<0, CH>([&]<int ch>() {
+                    hm[ch] = m[ch];
+                    hl[ch] = l[ch];
+                    static_for<0, DL>([&]<int e>() { hacc[ch][e] = acc[ch][e]; });
+                });
+                hslot = (int64_t)wave + unit;
+                return;
+            }
+        }
         store_segment((int64_t)wave + unit, m, l, acc);
     };
 
@@ -739,7 +761,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_multi_kernel(Mult
             });
         }
         finish_unit(cp, g);
-        if (g + 1 >= g1) break;
+        if (g + 1 >= g1) {
+            if constexpr (kHoldFirst) {
+                if (hslot >= 0) store_segment(hslot, hm, hl, hacc);
+            }
+            break;
+        }
         advance(cp);
         ++g;
         // the next sub-tiles sit in buffers brk + 1, brk + 2, ... (mod kMDepth):
