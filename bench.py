@@ -191,6 +191,20 @@ def timed(fn, n, stream):
     return e0.elapsed_time(e1) / n * 1e3
 
 
+def warm_up(fn, n):
+    """n untimed calls, then more until the GPU has been busy for about 0.2 s,
+    so that timed calls do not run at the clocks of an idle GPU."""
+    import torch
+    for k in range(n):
+        fn(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        for k in range(20):
+            fn(k)
+        torch.cuda.synchronize()
+
+
 def per_call(fn, n, stream):
     """p10 / median / p90 of per-call durations (an event pair around each call)."""
     import torch
@@ -232,9 +246,7 @@ def workload_line(name, dev, steps, warmup, nsets, stream):
     one workload, each back to back over its input copies."""
     import torch
     base, sets, outs, ws, calls = setup(name, dev, nsets)
-    for k in range(max(2, warmup)):
-        calls.step(k)
-    torch.cuda.synchronize()
+    warm_up(calls.step, max(2, warmup))
     step_us = timed(calls.step, steps, stream)
     sep_us = timed(calls.separate, steps, stream)
     dec_us = timed(calls.decode, steps, stream)
@@ -381,14 +393,7 @@ def main() -> int:
 
     # W untimed warmup steps, then more until the GPU has been busy for about
     # 0.2 s, so that the timed steps do not run at idle clocks
-    for k in range(Wm):
-        calls.step(k)
-    torch.cuda.synchronize()
-    t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < 0.2:
-        for k in range(50):
-            calls.step(k)
-        torch.cuda.synchronize()
+    warm_up(calls.step, Wm)
     w0 = time.perf_counter()
     step_us = timed(calls.step, K, stream)          # the timed region: K steps
     wall = time.perf_counter() - w0
@@ -420,8 +425,7 @@ def main() -> int:
         def multi_call(k):
             if lib.paged_attn_decode_multi(*margs[k % nsets]) != 0:
                 raise RuntimeError("paged_attn_decode_multi failed")
-        for k in range(3):
-            multi_call(k)
+        warm_up(multi_call, 3)
         multi_us = timed(multi_call, K, stream)
         extras["multi_query_decode"] = {
             "entry_point": f"paged_attn_decode_multi ({T} query tokens per sequence, causal)",
@@ -521,9 +525,7 @@ def shared_prefix_line(dev, steps, stream):
     def shared_call(k):
         if lib.paged_attn_decode_shared(*sargs[k % 4]) != 0:
             raise RuntimeError("paged_attn_decode_shared failed")
-    for k in range(3):
-        shared_call(k)
-    torch.cuda.synchronize()
+    warm_up(shared_call, 3)
     us = timed(shared_call, steps, stream)
     nbytes, unique = base.kv_read_bytes(), base.kv_unique_bytes()
     line = {"shared_decode": {
