@@ -20,8 +20,9 @@
  *   slot_mapping      int64 [num_tokens]; slot = physical_block*block_size + offset
  *
  * Ownership: every pointer argument is device memory owned by the caller.  The
- * library allocates nothing and is reentrant; its only global state is a cache
- * of the decode kernel's occupancy per configuration, filled on first use.  All
+ * library allocates nothing and is reentrant; its global state is caches filled
+ * on first use (kernel occupancy per configuration, compute units per device)
+ * and the per-device static array behind paged_decode_step_static.  All
  * work is queued asynchronously on `stream` (NULL = the null stream).  Outputs
  * are `out` and the caches; `out` must not alias q or the caches, and k/v must
  * not alias the caches.
@@ -30,8 +31,8 @@
  * only (no device reads, no synchronisation); a failed check returns before
  * anything is launched.  Preconditions on device-resident data are NOT checked
  * by the compute calls (paged_check_inputs checks them on request): block ids
- * used by a sequence lie in [0, num_blocks); non-negative slots are distinct
- * and below num_blocks*block_size; 0 <= context_lens[i] <= max_context_len.
+ * used by a sequence lie in [0, num_blocks); non-negative slots are distinct;
+ * 0 <= context_lens[i] <= max_context_len.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -75,7 +76,8 @@ int pkv_version(void);
  * For every token n with slot s = slot_mapping[n] >= 0 and every KV head h:
  *   k_cache[s / block_size, h, s % block_size, :] = k[n, h, :]   (bit copy)
  *   v_cache[s / block_size, h, s % block_size, :] = v[n, h, :]
- * A negative slot skips the token.  Defined by "PagedAttention核心思想" section
+ * A negative slot skips the token, and so does a slot at or past
+ * num_blocks*block_size (the kernel checks the bound).  Defined by "PagedAttention核心思想" section
  * 2.4.2 (a new token goes into the next slot of the last block; a fresh block
  * is taken only when the last one is full) and the CSDN answer's flow chart in
  * section 四 (append a page, update the mapping).
