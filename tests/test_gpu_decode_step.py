@@ -40,7 +40,7 @@ def check_step(inp, dtype, pairs=None, what=""):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_fused_step_small_shapes(dtype, D, G):
     say(f"case: fused step dtype={dtype} D={D} G={G}")
     lens = [0, 1, 2, 16, 17, 33, 255, 256, 257, 700]
@@ -55,7 +55,7 @@ def test_fused_step_small_shapes(dtype, D, G):
                        inp.v_new[1][g].view(torch.int16 if dtype != "f32" else torch.int32))
 
 
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
 def test_fused_step_block_sizes_and_boundaries(bs):
     say(f"case: fused step bs={bs}")
     lens = [bs - 1, bs, bs + 1, 2 * bs, 3 * bs + 5, 1000, 1024, 1025]
