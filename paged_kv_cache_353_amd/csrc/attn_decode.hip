@@ -71,6 +71,15 @@ constexpr int kUnitCost = PKV_UNIT_COST;
 #ifndef PKV_DEPTH
 #define PKV_DEPTH 2
 #endif
+// Ablation build only (-DPKV_QK_VALU=1, `python -m paged_kv_cache_353_amd.build
+// --qk-valu`): q.K on the VALU instead of the matrix cores, for bf16 at
+// head_dim 128 with up to 4 query heads per KV head -- each lane takes dot2
+// products over 8 dims of 4 K rows and four DPP steps sum the 16 lanes of a
+// row -- so that what MFMA saves can be measured.  The library itself is
+// built without it.
+#ifndef PKV_QK_VALU
+#define PKV_QK_VALU 0
+#endif
 constexpr int kDepth = PKV_DEPTH;  // sub-tiles in flight per wave
 
 // Position of a wave's load or compute stage in the (sequence, KV head,
@@ -253,6 +262,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // dims 64b + 16*(lane/16) bytes for load b); V rows 4*rg.. (see NL loads)
     const int koff = c * ROW + 16 * rg;
     const int voff = (4 * rg + (c / R)) * ROW + (c % R) * 16;
+    // ablation: K rows loaded like V rows (lane (r, c): row 4r + b, dims 8c..8c+7)
+    constexpr bool kQkValu = PKV_QK_VALU && std::is_same_v<DT, BF16> && R == 16 && NL >= G;
 
     // bytes from a cache's base to the first row of the sub-tile at `u`
     auto tile_offset = [&](const Cursor &u) __attribute__((always_inline)) -> int64_t {
@@ -284,7 +295,7 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         const int nbytes = uniform(rows * ROW);
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kc + off), 0, nbytes, kBufferFlags);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(vc + off), 0, nbytes, kBufferFlags);
-        static_for<0, NL>([&]<int b>() { kr[b] = load_stream(rk, koff + 64 * b); });
+        static_for<0, NL>([&]<int b>() { kr[b] = load_stream(rk, kQkValu ? voff + 256 * b : koff + 64 * b); });
         static_for<0, NL>([&]<int m>() { vr[m] = load_stream(rv, voff + 256 * m); });
         // keep the compute of the previous sub-tile (and its waits) after these
         // loads, so that they are in flight while it runs
@@ -310,7 +321,9 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         const __amdgpu_buffer_rsrc_t rvn = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(static_cast<const char *>(a.v_new) + nb), 0, ROW, kBufferFlags);
         // out-of-range offsets (negative ones wrap to huge) read as zero
-        static_for<0, NL>([&]<int b>() { knew[b] = load_chunk(rkn, koff - rn * ROW + 64 * b); });
+        static_for<0, NL>([&]<int b>() {
+            knew[b] = load_chunk(rkn, kQkValu ? voff - rn * ROW + 256 * b : koff - rn * ROW + 64 * b);
+        });
         static_for<0, NL>([&]<int m>() { vnew[m] = load_chunk(rvn, voff - rn * ROW + 256 * m); });
     };
 
@@ -326,7 +339,8 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         const char *qb = static_cast<const char *>(a.q) + uniform(((int64_t)u.seq * Hq + (int64_t)u.kvh * G) * ROW);
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb, 0, G * ROW, kBufferFlags);
         const int qoff = c * ROW + 16 * rg;  // head c (out of range, so zero, for c >= G)
-        static_for<0, NL>([&]<int b>() { qd[b] = load_chunk(rq, qoff + 64 * b); });
+        // (ablation: head b's dims 8c..8c+7 in load b)
+        static_for<0, NL>([&]<int b>() { qd[b] = load_chunk(rq, kQkValu ? b * ROW + c * 16 : qoff + 64 * b); });
     };
     auto reset_state = [&]() {
         m_run = kNegInf;
@@ -627,7 +641,34 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
     // One sub-tile: scores on MFMA, four-stream online softmax, acc += p V.
     auto process_rows = [&](int nvalid, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) __attribute__((always_inline)) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        static_for<0, NL>([&]<int b>() { s = mfma_chunk<DT>(kr[b], qr[b], s); });
+        if constexpr (kQkValu) {
+            typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+            auto bf2 = [](uint32_t u) __attribute__((always_inline)) { return __builtin_bit_cast(bf16x2v, u); };
+            float part[4][G];
+            static_for<0, 4>([&]<int r>() {
+                static_for<0, G>([&]<int h>() {
+                    float x = 0.f;
+                    static_for<0, 4>([&]<int i>() {
+                        const uint32_t ku = kr[r][i], qu = qr[h][i];
+                        x = __builtin_amdgcn_fdot2_f32_bf16(bf2(ku), bf2(qu), x, false);
+                    });
+                    // sum over the 16 lanes of the row: row_ror 8, row_ror 4, quad swaps
+                    x += as_f(__builtin_amdgcn_update_dpp(0, (int)as_u(x), 0x128, 0xF, 0xF, false));
+                    x += as_f(__builtin_amdgcn_update_dpp(0, (int)as_u(x), 0x124, 0xF, 0xF, false));
+                    x += as_f(__builtin_amdgcn_update_dpp(0, (int)as_u(x), 0x4E, 0xF, 0xF, false));
+                    x += as_f(__builtin_amdgcn_update_dpp(0, (int)as_u(x), 0xB1, 0xF, 0xF, false));
+                    part[r][h] = x;
+                });
+            });
+            // lane (r, c) keeps the score of token 4r + j for head c, as the MFMA leaves it
+            static_for<0, 4>([&]<int j>() {
+                float v = 0.f;
+                static_for<0, G>([&]<int h>() { v = c == h ? part[j][h] : v; });
+                s[j] = v;
+            });
+        } else {
+            static_for<0, NL>([&]<int b>() { s = mfma_chunk<DT>(kr[b], qr[b], s); });
+        }
         float sv[4];
         float tmax = kNegInf;
         static_for<0, 4>([&]<int r>() {
@@ -678,7 +719,12 @@ __global__ __launch_bounds__(kWavesPerGroup * kWave) void attn_stream_kernel(Dec
         char *kd = static_cast<char *>(a.k_cache_w) + so;
         char *vd = static_cast<char *>(a.v_cache_w) + so;
         static_for<0, NL>([&]<int b>() {
-            if (c == rn) store_chunk(kd, ROW, 16 * rg + 64 * b, knew[b]);
+            if constexpr (kQkValu) {
+                const int o = voff + 256 * b;
+                if (o / ROW == rn) store_chunk(kd, ROW, o - rn * ROW, knew[b]);
+            } else {
+                if (c == rn) store_chunk(kd, ROW, 16 * rg + 64 * b, knew[b]);
+            }
         });
         static_for<0, NL>([&]<int m>() {
             const int o = voff + 256 * m;
